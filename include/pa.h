@@ -1,0 +1,186 @@
+/*
+ * pa.h -- C ABI of libpa.so, paged KV-cache attention for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operations follow two pages:
+ *   [QbitAI] "DeepSeek研究员1200行代码复刻vLLM，H800硬件实测性能反超原版"
+ *            (163.com), section "vLLM是什么？": PagedAttention splits the KV
+ *            cache into fixed-size blocks, maps each sequence's logical blocks
+ *            to physical blocks through a block table, and the attention kernel
+ *            fetches each KV block separately.
+ *   [Report] "nano-vllm 深度分析报告" (nightvoyager): table "可复用的模式与技巧",
+ *            row "slot_mapping -1 padding" (padding positions carry -1 in
+ *            slot_mapping and the KV-store kernel skips them); table
+ *            "关键设计决策", row "block_size=256" (nano-vLLM uses 256-token
+ *            blocks where vLLM uses 16); section "创新之处" (prefix caching
+ *            shares cached blocks between sequences).
+ *
+ * Conventions shared by every call:
+ *   - Pointers named k, v, q, out, *_cache and workspace are DEVICE pointers
+ *     (hipMalloc'd or torch CUDA tensors). bf16 buffers are passed as void*:
+ *     each element is the 16-bit bfloat16 bit pattern. Metadata arrays
+ *     (slot_mapping, block_table, context_lens, cu_seqlens_q) are int32 device
+ *     arrays, except in pa_validate_metadata, which reads host arrays.
+ *   - KV pool layout (one pool for K, one for V):
+ *         [num_blocks][block_size][num_kv_heads][head_dim]   bf16, row-major.
+ *     Token slot s = physical_block * block_size + offset_in_block; the
+ *     (slot, kv_head) row of head_dim elements starts at element
+ *     (s * num_kv_heads + kv_head) * head_dim.
+ *   - GQA: query head h reads kv head h / (num_q_heads / num_kv_heads).
+ *   - The caller owns every buffer. No call allocates, frees or synchronises;
+ *     each one only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns. Kernel faults surface at the caller's next
+ *     synchronisation.
+ *   - Scalar arguments are checked on the host; a call that fails a check
+ *     enqueues nothing. Device metadata (block ids, slots, lengths) is NOT
+ *     read on the host: keeping it in range is the caller's contract, and
+ *     pa_validate_metadata checks a host copy of it.
+ *   - Supported shapes: head_dim == 128; block_size a power of two in
+ *     [16, 256]; num_q_heads / num_kv_heads in {1, 2, 4, 8}. bf16 device
+ *     buffers must be 16-byte aligned.
+ *   - All calls are safe to enqueue from several host threads on different
+ *     streams; there is no global state beyond the cached device properties.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-returning call. */
+#define PA_OK 0
+#define PA_ERR_NULL (-1)        /* a required pointer is NULL                   */
+#define PA_ERR_SHAPE (-2)       /* inconsistent or negative sizes, bad metadata */
+#define PA_ERR_UNSUPPORTED (-3) /* valid but unsupported shape or alignment     */
+#define PA_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required   */
+#define PA_ERR_HIP (-5)         /* the HIP runtime reported an error on launch  */
+
+/* Static text for a status code (never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * pa_store_kvcache -- write new tokens' K and V into the paged pools.
+ * [Report], table "可复用的模式与技巧", row "slot_mapping -1 padding".
+ *
+ *   For each token i in [0, num_tokens) with s = slot_mapping[i]:
+ *     s == -1 : nothing is written (a padding position);
+ *     s >= 0  : the num_kv_heads*head_dim bf16 words of k[i] and v[i] are
+ *               copied bit for bit to slot s of k_cache and v_cache.
+ *
+ *   k, v            [num_tokens][kv_token_stride] bf16; the first
+ *                   num_kv_heads*head_dim elements of each row are the token's
+ *                   K (resp. V) laid out [num_kv_heads][head_dim]. A stride
+ *                   larger than num_kv_heads*head_dim lets the caller pass
+ *                   slices of a fused QKV projection output. kv_token_stride
+ *                   must be a multiple of 8.
+ *   k_cache,v_cache pools, [num_blocks][block_size][num_kv_heads][head_dim].
+ *   slot_mapping    [num_tokens] int32, each -1 or in [0, num_blocks*block_size).
+ *   Two tokens naming the same slot is undefined (one of them wins).
+ *   num_tokens == 0 is valid and enqueues nothing.
+ */
+int pa_store_kvcache(const void* k, const void* v, int64_t kv_token_stride,
+                     void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                     int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                     int32_t num_kv_heads, int32_t head_dim, void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (the split-K
+ * partial results). 0 is never returned for a valid call with batch > 0.
+ */
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t block_size);
+
+/*
+ * pa_decode -- one query token per sequence attends over its paged context.
+ * [QbitAI], section "vLLM是什么？" (block-table addressed KV blocks).
+ *
+ *   For row b with L = context_lens[b] and query head h (kv head g = h/G):
+ *     key/value j in [0, L) live at slot
+ *        block_table[b*block_table_stride + j/block_size]*block_size + j%block_size;
+ *     s_j = scale * <q[b,h,:], K_j[g,:]>,
+ *     out[b,h,:] = sum_j softmax(s)_j V_j[g,:]      (fp32 math, bf16 RNE out).
+ *   L counts the new token, which must already be in the pool (store it with
+ *   pa_store_kvcache first, on the same stream). L == 0 marks a padding row:
+ *   its output is written as zeros and its block_table row is not read.
+ *
+ *   out, q          [batch][num_q_heads][head_dim] bf16.
+ *   block_table     [batch][block_table_stride] int32; only the first
+ *                   ceil(L/block_size) entries of a row are read.
+ *   context_lens    [batch] int32, each in [0, max_context_len].
+ *   max_context_len host-side upper bound of context_lens (sizes the grid);
+ *                   ceil(max_context_len/block_size) <= block_table_stride.
+ *   workspace       device scratch of at least pa_decode_workspace_bytes(...)
+ *                   bytes, 256-byte aligned; its contents need no
+ *                   initialisation and are garbage afterwards. Two calls in
+ *                   flight at once must not share a workspace.
+ *   The result is bitwise independent of which physical blocks hold the
+ *   context (the summation order follows logical positions only).
+ */
+int pa_decode(void* out, const void* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_table,
+              int32_t block_table_stride, const int32_t* context_lens,
+              int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t block_size, int32_t max_context_len,
+              float scale, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
+ * pa_prefill_varlen -- causal attention for a batch of variable-length
+ * prompts whose leading blocks may come from the prefix cache.
+ * [QbitAI] "vLLM是什么？" (paging) and [Report] "创新之处" (prefix caching).
+ *
+ *   Sequence b owns query rows t in [cu_seqlens_q[b], cu_seqlens_q[b+1]):
+ *   its N_b new tokens. Its context holds L_b = context_lens[b] tokens: a
+ *   cached prefix of P_b = L_b - N_b tokens followed by the new ones, all
+ *   already in the pool (store the new ones with pa_store_kvcache first).
+ *   New row i (0-based) sits at position P_b + i and sees keys 0 .. P_b + i
+ *   (causal mask aligned to the end of the context):
+ *     out[t,h,:] = sum_{j <= P_b+i} softmax(scale*<q[t,h,:],K_j[g,:]>) V_j[g,:].
+ *
+ *   out, q          [total_q][num_q_heads][head_dim] bf16,
+ *                   total_q == cu_seqlens_q[batch].
+ *   cu_seqlens_q    [batch+1] int32, non-decreasing, cu_seqlens_q[0] == 0.
+ *   context_lens    [batch] int32, context_lens[b] >= N_b.
+ *   block_table     [batch][block_table_stride] int32.
+ *   max_seqlen_q    host-side upper bound of every N_b (sizes the grid).
+ *   A sequence with N_b == 0 produces no rows.
+ */
+int pa_prefill_varlen(void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* cu_seqlens_q,
+                      const int32_t* context_lens, const int32_t* block_table,
+                      int32_t block_table_stride, int32_t batch,
+                      int32_t total_q, int32_t max_seqlen_q,
+                      int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, float scale,
+                      void* stream);
+
+/*
+ * pa_validate_metadata -- host-side check of the metadata contract.
+ * All pointers are HOST arrays; nothing touches the GPU. Checks that every
+ * context length is in [0, max_context_len] (max_context_len < 0 skips that
+ * bound), that every block-table entry a row reads is in [0, num_blocks), that
+ * no physical block is read by a row twice, that slot_mapping entries are -1
+ * or in [0, num_blocks*block_size) with no valid slot repeated, and, when
+ * cu_seqlens_q is given, that it is non-decreasing from 0 with
+ * N_b <= context_lens[b]. cu_seqlens_q and slot_mapping may be NULL.
+ * Returns PA_OK or PA_ERR_SHAPE; on failure writes a message into `detail`
+ * (if non-NULL, up to detail_len bytes including the terminator).
+ */
+int pa_validate_metadata(const int32_t* block_table, int32_t block_table_stride,
+                         const int32_t* context_lens, int32_t batch,
+                         const int32_t* cu_seqlens_q,
+                         const int32_t* slot_mapping, int32_t num_slots,
+                         int32_t num_blocks, int32_t block_size,
+                         int32_t max_context_len, char* detail,
+                         size_t detail_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,196 @@
+"""Paged KV-cache attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libpa.so (C ABI in include/pa.h). Each function has
+the name of the C entry point it calls and only marshals arguments: torch
+tensors become device pointers and sizes, and the stream defaults to torch's
+current stream. Every step of the computation runs in the HIP kernels of
+libpa.so; there is no fallback. If libpa.so has not been built, every call
+raises.
+
+  pa_store_kvcache   write new tokens' K/V into the paged pools (slot -1 skipped)
+  pa_decode          one query token per sequence over its paged context
+  pa_prefill_varlen  causal varlen prefill over a cached prefix plus new tokens
+"""
+import ctypes
+import os
+
+__all__ = ["PAError", "library", "lib_path", "pa_store_kvcache", "pa_decode",
+           "pa_decode_workspace_bytes", "pa_prefill_varlen", "pa_validate_metadata",
+           "pa_status_string", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libpa.so")
+
+EXPORTED_SYMBOLS = ("pa_status_string", "pa_store_kvcache", "pa_decode_workspace_bytes",
+                    "pa_decode", "pa_prefill_varlen", "pa_validate_metadata")
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    """A libpa.so call returned a non-zero status."""
+
+    def __init__(self, name, status, detail=""):
+        self.status = status
+        msg = f"{name}: {pa_status_string(status)} (status {status})"
+        super().__init__(msg + (f": {detail}" if detail else ""))
+
+
+def library():
+    """The loaded libpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with "
+                               "`python -m paged_kv_cache_slot_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(lib_path)
+        p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.pa_status_string.argtypes = [ctypes.c_int]
+        lib.pa_status_string.restype = ctypes.c_char_p
+        lib.pa_store_kvcache.argtypes = [p, p, i64, p, p, p, i32, i32, i32, i32, i32, p]
+        lib.pa_store_kvcache.restype = ctypes.c_int
+        lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.pa_decode_workspace_bytes.restype = sz
+        lib.pa_decode.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i32,
+                                  ctypes.c_float, p, sz, p]
+        lib.pa_decode.restype = ctypes.c_int
+        lib.pa_prefill_varlen.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, ctypes.c_float, p]
+        lib.pa_prefill_varlen.restype = ctypes.c_int
+        lib.pa_validate_metadata.argtypes = [p, i32, p, i32, p, p, i32, i32, i32, i32,
+                                             ctypes.c_char_p, sz]
+        lib.pa_validate_metadata.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def pa_status_string(status):
+    return library().pa_status_string(int(status)).decode()
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    """Device pointer of a tensor (None -> NULL), after checking where it lives."""
+    if t is None:
+        return None
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, rc):
+    if rc != 0:
+        raise PAError(name, rc)
+
+
+def _pool_shape(k_cache, v_cache):
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, Hkv, D]")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("pools must be contiguous")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def pa_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    """k, v: [T, Hkv, D] or [T, >= Hkv*D] bf16 with unit stride inside a row
+    (row slices of a fused QKV buffer are fine); pools [NB, bs, Hkv, D];
+    slot_mapping [T] int32 (-1 = skip)."""
+    import torch
+    num_blocks, bs, hkv, d = _pool_shape(k_cache, v_cache)
+    T = int(k.shape[0])
+    k2 = k.flatten(1) if k.dim() == 3 else k
+    v2 = v.flatten(1) if v.dim() == 3 else v
+    if k2.dim() != 2 or k2.stride(1) != 1 or v2.stride(1) != 1 or k2.stride(0) != v2.stride(0):
+        raise ValueError("k and v rows must have unit element stride and equal row strides")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    rc = library().pa_store_kvcache(
+        _dev(k2, "k", torch.bfloat16), _dev(v2, "v", torch.bfloat16), int(k2.stride(0)),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(slot_mapping, "slot_mapping", torch.int32), T, num_blocks, bs, hkv, d,
+        _stream(stream))
+    _check("pa_store_kvcache", rc)
+
+
+def pa_decode_workspace_bytes(batch, num_q_heads, head_dim, max_context_len, block_size):
+    return int(library().pa_decode_workspace_bytes(batch, num_q_heads, head_dim,
+                                                   max_context_len, block_size))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, scale,
+              workspace, stream=None):
+    """out, q: [B, Hq, D] bf16; block_table [B, stride] int32; context_lens [B] int32;
+    workspace: a uint8 GPU tensor of at least pa_decode_workspace_bytes(...) bytes."""
+    import torch
+    num_blocks, bs, hkv, d = _pool_shape(k_cache, v_cache)
+    B, hq, dq = (int(x) for x in q.shape)
+    if out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("out and q must be contiguous [B, Hq, D]")
+    if not block_table.is_contiguous() or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be a contiguous [B, stride] int32 tensor")
+    rc = library().pa_decode(
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), B, hq, hkv, dq, bs,
+        int(max_context_len), float(scale), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream))
+    _check("pa_decode", rc)
+
+
+def pa_prefill_varlen(out, q, k_cache, v_cache, cu_seqlens_q, context_lens, block_table,
+                      max_seqlen_q, scale, stream=None):
+    """out, q: [total_q, Hq, D] bf16; cu_seqlens_q [B+1], context_lens [B],
+    block_table [B, stride] int32."""
+    import torch
+    num_blocks, bs, hkv, d = _pool_shape(k_cache, v_cache)
+    T, hq, dq = (int(x) for x in q.shape)
+    B = int(context_lens.shape[0])
+    if out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("out and q must be contiguous [total_q, Hq, D]")
+    if cu_seqlens_q.numel() != B + 1 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("cu_seqlens_q must be [B+1] and block_table [B, stride]")
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous")
+    rc = library().pa_prefill_varlen(
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]), B, T,
+        int(max_seqlen_q), hq, hkv, dq, bs, float(scale), _stream(stream))
+    _check("pa_prefill_varlen", rc)
+
+
+def pa_validate_metadata(block_table, context_lens, num_blocks, block_size, cu_seqlens_q=None,
+                         slot_mapping=None, max_context_len=-1):
+    """Host-side metadata check (numpy or CPU tensors). Raises PAError with the
+    library's message on the first violation."""
+    import numpy as np
+
+    def arr(a):
+        if a is None:
+            return None
+        if hasattr(a, "detach"):
+            a = a.detach().cpu().numpy()
+        return np.ascontiguousarray(a, dtype=np.int32)
+
+    bt, cl, cu, sm = arr(block_table), arr(context_lens), arr(cu_seqlens_q), arr(slot_mapping)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+    msg = ctypes.create_string_buffer(256)
+    rc = library().pa_validate_metadata(
+        ptr(bt), int(bt.shape[1]) if bt is not None and bt.ndim == 2 else 0, ptr(cl),
+        int(len(cl)), ptr(cu), ptr(sm), 0 if sm is None else int(len(sm)), int(num_blocks),
+        int(block_size), int(max_context_len), msg, 256)
+    if rc != 0:
+        raise PAError("pa_validate_metadata", rc, msg.value.decode())

@@ -1,0 +1,202 @@
+// C ABI of libpa.so: host-side argument checks, then kernel launches on the
+// caller's stream. Nothing here allocates, frees or synchronises. The
+// operations and their sources are documented in include/pa.h.
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_block_size(int32_t bs) { return bs >= 16 && bs <= 256 && (bs & (bs - 1)) == 0; }
+
+bool supported_group(int32_t hq, int32_t hkv) {
+  const int32_t g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Checks shared by decode and prefill. Returns PA_OK or the first failure.
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (head_dim != pa::kHeadDim || !supported_block_size(block_size) ||
+      !supported_group(num_q_heads, num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+void write_detail(char* detail, size_t len, const char* msg) {
+  if (detail && len > 0) {
+    std::strncpy(detail, msg, len - 1);
+    detail[len - 1] = '\0';
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent or negative sizes";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int pa_store_kvcache(const void* k, const void* v, int64_t kv_token_stride, void* k_cache,
+                     void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                     int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                     int32_t head_dim, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (kv_token_stride < static_cast<int64_t>(num_kv_heads) * head_dim) return PA_ERR_SHAPE;
+  if (head_dim != pa::kHeadDim || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  if (kv_token_stride % 8 != 0 || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  return from_hip(pa::launch_store_kvcache(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), kv_token_stride,
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), slot_mapping, num_tokens,
+      num_kv_heads, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t block_size) {
+  (void)head_dim;
+  (void)block_size;
+  if (batch <= 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
+  return pa::decode_workspace_bytes(batch, num_q_heads, max_context_len);
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, int32_t block_table_stride,
+              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  if (batch < 0 || max_context_len < 0 || block_table_stride < 0) return PA_ERR_SHAPE;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (static_cast<int64_t>(block_table_stride) * block_size < max_context_len)
+    return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const size_t need = pa::decode_workspace_bytes(batch, num_q_heads, max_context_len);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+  return from_hip(pa::launch_decode(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table,
+      block_table_stride, context_lens, batch, num_q_heads, num_kv_heads, block_size,
+      max_context_len, scale, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                      const int32_t* block_table, int32_t block_table_stride, int32_t batch,
+                      int32_t total_q, int32_t max_seqlen_q, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                      void* stream) {
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || block_table_stride <= 0)
+    return PA_ERR_SHAPE;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !cu_seqlens_q || !context_lens || !block_table)
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  return from_hip(pa::launch_prefill(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), cu_seqlens_q,
+      context_lens, block_table, block_table_stride, batch, max_seqlen_q, num_q_heads,
+      num_kv_heads, block_size, scale, static_cast<hipStream_t>(stream)));
+}
+
+int pa_validate_metadata(const int32_t* block_table, int32_t block_table_stride,
+                         const int32_t* context_lens, int32_t batch, const int32_t* cu_seqlens_q,
+                         const int32_t* slot_mapping, int32_t num_slots, int32_t num_blocks,
+                         int32_t block_size, int32_t max_context_len, char* detail,
+                         size_t detail_len) {
+  char msg[256];
+  auto fail = [&](const char* text) {
+    write_detail(detail, detail_len, text);
+    return PA_ERR_SHAPE;
+  };
+  if (batch < 0 || num_slots < 0 || num_blocks < 0 || block_size <= 0 || block_table_stride < 0)
+    return fail("negative size");
+  if (batch > 0 && (!block_table || !context_lens)) return fail("block_table or context_lens is NULL");
+  if (num_slots > 0 && !slot_mapping) return fail("slot_mapping is NULL");
+  std::vector<int32_t> seen(static_cast<size_t>(num_blocks), -1);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t L = context_lens[b];
+    if (L < 0 || (max_context_len >= 0 && L > max_context_len)) {
+      std::snprintf(msg, sizeof msg, "context_lens[%d] = %d out of range", b, L);
+      return fail(msg);
+    }
+    const int64_t nblk = (static_cast<int64_t>(L) + block_size - 1) / block_size;
+    if (nblk > block_table_stride) {
+      std::snprintf(msg, sizeof msg, "row %d needs %lld blocks > block_table_stride %d", b,
+                    static_cast<long long>(nblk), block_table_stride);
+      return fail(msg);
+    }
+    for (int64_t j = 0; j < nblk; ++j) {
+      const int32_t p = block_table[static_cast<int64_t>(b) * block_table_stride + j];
+      if (p < 0 || p >= num_blocks) {
+        std::snprintf(msg, sizeof msg, "block_table[%d][%lld] = %d out of [0, %d)", b,
+                      static_cast<long long>(j), p, num_blocks);
+        return fail(msg);
+      }
+      if (seen[p] == b) {
+        std::snprintf(msg, sizeof msg, "row %d reads physical block %d twice", b, p);
+        return fail(msg);
+      }
+      seen[p] = b;
+    }
+    if (cu_seqlens_q) {
+      if (b == 0 && cu_seqlens_q[0] != 0) return fail("cu_seqlens_q[0] != 0");
+      const int32_t n = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+      if (n < 0 || n > L) {
+        std::snprintf(msg, sizeof msg, "sequence %d has %d new tokens and context %d", b, n, L);
+        return fail(msg);
+      }
+    }
+  }
+  if (num_slots > 0) {
+    const int64_t total = static_cast<int64_t>(num_blocks) * block_size;
+    std::vector<uint8_t> used(static_cast<size_t>(total), 0);
+    for (int32_t i = 0; i < num_slots; ++i) {
+      const int32_t s = slot_mapping[i];
+      if (s == -1) continue;
+      if (s < 0 || s >= total) {
+        std::snprintf(msg, sizeof msg, "slot_mapping[%d] = %d out of range", i, s);
+        return fail(msg);
+      }
+      if (used[s]) {
+        std::snprintf(msg, sizeof msg, "slot %d named twice in slot_mapping", s);
+        return fail(msg);
+      }
+      used[s] = 1;
+    }
+  }
+  write_detail(detail, detail_len, "ok");
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+"""The C-ABI library on the host: it loads, exports what include/pa.h declares,
+and rejects bad arguments before touching the GPU. No kernel runs here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_slot_amd as pa
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.lib_path):
+        pytest.fail("libpa.so is not built (run __graft_entry__.build())")
+    return pa.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(pa.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pa_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, -5):
+        assert pa.pa_status_string(code) not in ("", "unknown status")
+    assert pa.pa_status_string(1234) == "unknown status"
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)   # never dereferenced: every call below fails a host check
+
+
+def test_store_argument_checks(lib):
+    f = lib.pa_store_kvcache
+    P = _fake()
+    assert f(None, None, 1024, None, None, None, 0, 10, 256, 8, 128, None) == PA_OK  # nothing to do
+    assert f(P, P, 1024, P, P, None, 4, 10, 256, 8, 128, None) == PA_ERR_NULL
+    assert f(P, P, 1024, P, P, P, -1, 10, 256, 8, 128, None) == PA_ERR_SHAPE
+    assert f(P, P, 1000, P, P, P, 4, 10, 256, 8, 128, None) == PA_ERR_SHAPE  # stride < row
+    assert f(P, P, 512, P, P, P, 4, 10, 256, 8, 64, None) == PA_ERR_UNSUPPORTED  # head_dim
+    assert f(P, P, 1024, P, P, P, 4, 10, 100, 8, 128, None) == PA_ERR_UNSUPPORTED  # block size
+    assert f(P, P, 1028, P, P, P, 4, 10, 256, 8, 128, None) == PA_ERR_UNSUPPORTED  # stride % 8
+    assert f(_fake(0x10002), P, 1024, P, P, P, 4, 10, 256, 8, 128, None) == PA_ERR_UNSUPPORTED
+
+
+def test_decode_argument_checks(lib):
+    f = lib.pa_decode
+    P = _fake()
+    ws = pa.pa_decode_workspace_bytes(4, 16, 128, 300, 256)
+    base = dict(out=P, q=P, kc=P, vc=P, bt=P, stride=2, cl=P, B=4, hq=16, hkv=8, d=128, bs=256,
+                maxl=300, scale=0.088, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["stride"], a["cl"], a["B"],
+                 a["hq"], a["hkv"], a["d"], a["bs"], a["maxl"], a["scale"], a["ws"], a["wsb"], None)
+
+    assert call(B=0) == PA_OK
+    assert call(q=None) == PA_ERR_NULL
+    assert call(hq=12) == PA_ERR_SHAPE            # 12 % 8 != 0
+    assert call(hq=24, hkv=8) == PA_ERR_UNSUPPORTED  # G = 3
+    assert call(hq=128, hkv=8) == PA_ERR_UNSUPPORTED  # G = 16
+    assert call(d=64) == PA_ERR_UNSUPPORTED
+    assert call(bs=8) == PA_ERR_UNSUPPORTED
+    assert call(stride=1) == PA_ERR_SHAPE         # 1 block cannot hold 300 tokens
+    assert call(wsb=ws - 1) == PA_ERR_WORKSPACE
+    assert call(ws=None) == PA_ERR_WORKSPACE
+    assert call(maxl=-1) == PA_ERR_SHAPE
+
+
+def test_prefill_argument_checks(lib):
+    f = lib.pa_prefill_varlen
+    P = _fake()
+    assert f(P, P, P, P, P, P, P, 4, 0, 0, 0, 32, 8, 128, 256, 0.1, None) == PA_OK
+    assert f(P, None, P, P, P, P, P, 4, 2, 10, 8, 32, 8, 128, 256, 0.1, None) == PA_ERR_NULL
+    assert f(P, P, P, P, P, P, P, 4, 2, 10, 8, 32, 8, 96, 256, 0.1, None) == PA_ERR_UNSUPPORTED
+    assert f(P, P, P, P, P, P, P, 4, 2, 10, 8, 30, 8, 128, 256, 0.1, None) == PA_ERR_SHAPE
+    assert f(P, P, P, P, P, P, P, 0, 2, 10, 8, 32, 8, 128, 256, 0.1, None) == PA_ERR_SHAPE
+
+
+def test_workspace_size():
+    # One fp32 (acc[128], max, sum) record per (row, query head, 256-token piece).
+    assert pa.pa_decode_workspace_bytes(256, 16, 128, 2048, 256) == 256 * 16 * 8 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(3, 4, 128, 0, 16) == 3 * 4 * 1 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(3, 4, 128, 257, 16) == 3 * 4 * 2 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(0, 4, 128, 257, 16) == 0
+
+
+@pytest.mark.parametrize("cid", [1, 4])
+def test_validate_metadata_accepts_generated(cid):
+    case = workloads.config_case(cid, **({} if cid == 1 else dict(batch=12)))
+    pa.pa_validate_metadata(case["block_table"], case["context_lens"], case["num_blocks"],
+                            case["block_size"], cu_seqlens_q=case.get("cu_seqlens_q"),
+                            slot_mapping=case["slot_mapping"])
+
+
+def test_validate_metadata_rejects():
+    case = workloads.config_case(3, batch=20, pad=2)
+    bt = case["block_table"].numpy().copy()
+    cl = case["context_lens"].numpy().copy()
+    sm = case["slot_mapping"].numpy().copy()
+    nb, bs = case["num_blocks"], case["block_size"]
+    pa.pa_validate_metadata(bt, cl, nb, bs, slot_mapping=sm, max_context_len=int(cl.max()))
+    bad = bt.copy(); bad[0, 0] = nb
+    with pytest.raises(pa.PAError, match="out of"):
+        pa.pa_validate_metadata(bad, cl, nb, bs)
+    bad = bt.copy(); bad[1, 0] = bad[0, 0]
+    with pytest.raises(pa.PAError):  # noqa: PT012 - two rows may share a block, a row may not repeat
+        b2 = bt.copy(); b2[0, 1] = b2[0, 0]
+        pa.pa_validate_metadata(b2, np.maximum(cl, bs + 1), nb, bs)
+    pa.pa_validate_metadata(bad, cl, nb, bs)   # shared between rows: allowed (prefix caching)
+    s2 = sm.copy(); s2[3] = s2[4] if s2[4] >= 0 else s2[5]
+    with pytest.raises(pa.PAError, match="twice"):
+        pa.pa_validate_metadata(bt, cl, nb, bs, slot_mapping=s2)
+    with pytest.raises(pa.PAError, match="context_lens"):
+        pa.pa_validate_metadata(bt, cl, nb, bs, max_context_len=int(cl.max()) - 1)
+    cu = np.array([0, 5, 3] + [3] * 18, dtype=np.int32)
+    with pytest.raises(pa.PAError, match="new tokens"):
+        pa.pa_validate_metadata(bt, cl, nb, bs, cu_seqlens_q=cu)

@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+KV stores must be bit-exact over the whole pool. Attention must satisfy
+|gpu - oracle| <= 1e-2 + 1e-2 |oracle| element-wise, with the oracle in fp64.
+Full-size workloads are checked on sampled rows the oracle computes one by one;
+small cases that still span several tiles and ragged tails are checked on
+every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_slot_amd as pa
+import workloads
+from tests.gpu_common import (DEV, compare, gpu_decode, gpu_prefill, gpu_store, host_copy,
+                              make_config, oracle_after_store, require_gpu, sample_rows, say,
+                              ORACLE_THREADS)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _pool_bits(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ store --
+
+@pytest.mark.parametrize("cid", [1, 3, 5, 4])
+def test_store_bit_exact_full_pool(cid):
+    """Whole-pool memcmp after the store, -1 rows included (configs 3 and 5 pad)."""
+    case, h = make_config(cid)
+    say(f"  pa_store_kvcache T={case['slot_mapping'].numel()} "
+        f"(-1 rows: {int((h['slot_mapping'] < 0).sum())})")
+    gpu_store(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    assert np.array_equal(_pool_bits(case["k_cache"]), kc), "K pool differs from the oracle"
+    assert np.array_equal(_pool_bits(case["v_cache"]), vc), "V pool differs from the oracle"
+    # The store must have changed every named slot (the pool held other data).
+    named = h["slot_mapping"][h["slot_mapping"] >= 0].numpy()
+    before = _pool_bits(h["k_cache"]).reshape(-1, h["num_kv_heads"] * 128)
+    assert not np.array_equal(before[named], kc.reshape(-1, h["num_kv_heads"] * 128)[named])
+
+
+def test_store_fused_qkv_rows():
+    """k and v as row slices of a fused [T, (Hq + 2 Hkv) * D] projection output."""
+    T, hq, hkv, d, nb, bs = 300, 32, 8, 128, 24, 16
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    fused = torch.randn(T, (hq + 2 * hkv) * d, generator=gen, device=DEV).to(torch.bfloat16)
+    kc = torch.randn(nb, bs, hkv, d, generator=gen, device=DEV).to(torch.bfloat16)
+    vc = torch.randn(nb, bs, hkv, d, generator=gen, device=DEV).to(torch.bfloat16)
+    rng = np.random.default_rng(5)
+    slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int32)
+    slots[rng.choice(T, size=30, replace=False)] = -1
+    k = fused[:, hq * d:(hq + hkv) * d]
+    v = fused[:, (hq + hkv) * d:]
+    h = dict(k=k.cpu(), v=v.cpu(), kc=kc.cpu(), vc=vc.cpu())
+    say("  pa_store_kvcache fused rows, T=300, bs=16")
+    pa.pa_store_kvcache(k, v, kc, vc, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    ek, ev = oracle.store_kvcache(h["k"], h["v"], h["kc"], h["vc"], slots, bs)
+    assert np.array_equal(_pool_bits(kc), ek) and np.array_equal(_pool_bits(vc), ev)
+
+
+def test_store_empty_is_noop():
+    kc = torch.zeros(2, 16, 8, 128, dtype=torch.bfloat16, device=DEV)
+    e = torch.empty(0, 8, 128, dtype=torch.bfloat16, device=DEV)
+    pa.pa_store_kvcache(e, e, kc, kc.clone(), torch.empty(0, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert int(kc.abs().sum()) == 0
+
+
+# ----------------------------------------------------------------- decode --
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+def test_decode_step_full_size(cid):
+    """store + decode on the full workload; every row for config 1, sampled rows
+    (longest, shortest, padding, 40 random) for the others."""
+    case, h = make_config(cid)
+    say(f"  pa_store_kvcache + pa_decode B={case['batch']} Hq={case['num_q_heads']} "
+        f"Hkv={case['num_kv_heads']} bs={case['block_size']} max_len={case['max_context_len']}")
+    gpu_store(case)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    rows = None if cid == 1 else sample_rows(h["lens"], 40, seed=cid)
+    ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
+                        rows=rows, nthreads=ORACLE_THREADS)
+    compare(out, ref, f"config {cid} decode", rows=rows)
+    pad = np.flatnonzero(h["lens"] == 0)
+    if len(pad):
+        assert int(out[torch.from_numpy(pad).to(DEV)].float().abs().sum()) == 0
+
+
+DECODE_GRID = [
+    # (block_size, Hq, Hkv, lengths)
+    (16, 32, 8, [1, 15, 16, 17, 255, 256, 257, 600, 1023, 0, 2048, 333]),
+    (256, 16, 8, [1, 255, 256, 257, 511, 512, 513, 0, 1100, 77]),
+    (32, 8, 8, [3, 64, 700, 129, 1, 256]),
+    (64, 16, 2, [5, 300, 1000, 0, 640]),
+    (128, 32, 4, [100, 1500, 260, 1]),
+    (16, 64, 8, [1, 17, 290, 513, 40]),
+]
+
+
+@pytest.mark.parametrize("bs,hq,hkv,lens", DECODE_GRID,
+                         ids=[f"bs{a}-hq{b}-hkv{c}" for a, b, c, _ in DECODE_GRID])
+def test_decode_grid_all_rows(bs, hq, hkv, lens):
+    """Several 256-token pieces, ragged tails, padding rows, every GQA ratio."""
+    say(f"[case] decode grid bs={bs} Hq={hq} Hkv={hkv} lens={lens}")
+    case = workloads.decode_case(len(lens), (1, 2048), hq, hkv, 128, bs, seed=77 + bs + hq,
+                                 device=DEV, lens=lens, spare_blocks=5)
+    h = host_copy(case)
+    gpu_store(case)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
+                        nthreads=ORACLE_THREADS)
+    compare(out, ref, "decode grid")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert int(out[b].float().abs().sum()) == 0
+
+
+def test_decode_max_context_len_above_all_rows():
+    """A loose max_context_len (more pieces than any row needs) changes nothing."""
+    lens = [40, 300, 0, 513]
+    case = workloads.decode_case(4, (1, 2048), 16, 8, 128, 16, seed=3, device=DEV, lens=lens)
+    tight = gpu_decode(case)
+    loose = gpu_decode(case, max_context_len=2048)
+    torch.cuda.synchronize()
+    assert torch.equal(tight, loose)
+
+
+def test_decode_all_padding_and_empty_batch():
+    case = workloads.decode_case(3, (1, 10), 16, 8, 128, 256, seed=4, device=DEV, lens=[0, 0, 0],
+                                 spare_blocks=1)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    assert int(out.float().abs().sum()) == 0
+    e = torch.empty(0, 16, 128, dtype=torch.bfloat16, device=DEV)
+    pa.pa_decode(e, e, case["k_cache"], case["v_cache"],
+                 torch.empty(0, 1, dtype=torch.int32, device=DEV),
+                 torch.empty(0, dtype=torch.int32, device=DEV), 0, 0.1, None)
+
+
+def test_decode_block_permutation_bitwise():
+    """Relabelling physical blocks (pool and table together) changes no output bit."""
+    lens = [1000, 17, 256, 2048, 513]
+    for bs in (16, 256):
+        case = workloads.decode_case(5, (1, 2048), 32, 8, 128, bs, seed=9, device=DEV, lens=lens,
+                                     spare_blocks=7)
+        out1 = gpu_decode(case)
+        nb = case["num_blocks"]
+        perm = torch.from_numpy(np.random.default_rng(9).permutation(nb)).to(DEV)
+        kc2 = torch.empty_like(case["k_cache"]); kc2[perm] = case["k_cache"]
+        vc2 = torch.empty_like(case["v_cache"]); vc2[perm] = case["v_cache"]
+        bt = case["block_table"]
+        bt2 = torch.where(bt >= 0, perm.to(torch.int32)[bt.clamp(min=0).long()], bt)
+        out2 = gpu_decode(dict(case, k_cache=kc2, v_cache=vc2, block_table=bt2.contiguous()))
+        torch.cuda.synchronize()
+        assert torch.equal(out1, out2), f"bs={bs}: permutation changed bits"
+
+
+def test_decode_deterministic():
+    case = workloads.config_case(1, device=DEV)
+    a = gpu_decode(case)
+    b = gpu_decode(case)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- prefill --
+
+def test_prefill_full_size_sampled():
+    """Config 4 (64 sequences, cached prefixes from 8 shared chains): store the
+    new tokens, run prefill, check 160 sampled query rows (all heads)."""
+    case, h = make_config(4)
+    say(f"  pa_store_kvcache + pa_prefill_varlen T={case['total_q']} "
+        f"max_seqlen_q={case['max_seqlen_q']}")
+    gpu_store(case)
+    out = gpu_prefill(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    rng = np.random.default_rng(44)
+    cu = h["cu_seqlens_q"].numpy()
+    toks = set(int(x) for x in rng.choice(case["total_q"], size=120, replace=False))
+    for b in rng.choice(case["batch"], size=10, replace=False):   # first and last rows
+        toks |= {int(cu[b]), int(cu[b + 1] - 1)}
+    toks = np.array(sorted(toks), dtype=np.int32)
+    ref = oracle.prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["context_lens"], h["block_table"],
+                         h["scale"], tokens=toks, nthreads=ORACLE_THREADS)
+    compare(out, ref, "config 4 prefill", rows=toks)
+
+
+PREFILL_GRID = [
+    # (block_size, Hq, Hkv, new lengths, prefix blocks)
+    (256, 32, 8, [100, 1, 33, 64, 257, 31], [0, 1, 3, 2, 1, 0]),
+    (16, 32, 8, [50, 1, 128, 97], [3, 0, 1, 2]),
+    (16, 16, 16, [200, 5, 129], [1, 2, 0]),
+    (64, 16, 8, [70, 300, 2], [2, 0, 1]),
+    (32, 64, 8, [40, 17, 90], [1, 3, 0]),
+    (16, 8, 4, [1, 1, 2, 3], [0, 3, 1, 2]),
+]
+
+
+@pytest.mark.parametrize("bs,hq,hkv,new,pre", PREFILL_GRID,
+                         ids=[f"bs{a}-hq{b}-hkv{c}" for a, b, c, _, _ in PREFILL_GRID])
+def test_prefill_grid_all_rows(bs, hq, hkv, new, pre):
+    """Every GQA ratio, prefixes that end mid key-tile, ragged query tiles, N = 1."""
+    say(f"[case] prefill grid bs={bs} Hq={hq} Hkv={hkv} new={new} prefix_blocks={pre}")
+    case = workloads.prefill_case(len(new), (1, 1024), hq, hkv, 128, bs, seed=500 + bs + hq,
+                                  device=DEV, chains=2, chain_blocks=3, new_lens=new,
+                                  prefix_blocks=pre, prefix_chain=[i % 2 for i in range(len(new))])
+    h = host_copy(case)
+    gpu_store(case)
+    out = gpu_prefill(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    ref = oracle.prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["context_lens"], h["block_table"],
+                         h["scale"], nthreads=ORACLE_THREADS)
+    compare(out, ref, "prefill grid")
+
+
+def test_prefill_row_matches_gpu_decode():
+    """Prefill row i of a sequence with prefix P equals decode with L = P + i + 1."""
+    case = workloads.prefill_case(1, (1, 1024), 32, 8, 128, 16, seed=61, device=DEV, chains=1,
+                                  chain_blocks=3, new_lens=[150], prefix_blocks=[3],
+                                  prefix_chain=[0])
+    gpu_store(case)
+    pre = gpu_prefill(case)
+    P = 48
+    rows = [0, 1, 15, 16, 63, 64, 100, 149]
+    dec_case = dict(case, q=case["q"][rows].contiguous(),
+                    block_table=case["block_table"].expand(len(rows), -1).contiguous(),
+                    context_lens=torch.tensor([P + i + 1 for i in rows], dtype=torch.int32,
+                                              device=DEV),
+                    max_context_len=P + 150)
+    dec = gpu_decode(dec_case)
+    torch.cuda.synchronize()
+    diff = (pre[rows].float() - dec.float()).abs()
+    assert float(diff.max()) <= 2e-2, float(diff.max())
+
+
+def test_prefill_shared_prefix_rows_identical():
+    """Two sequences on the same 2 physical prefix blocks, recomputed in full
+    (P = 0) with identical query rows there: identical output bits there."""
+    bs, hq, hkv = 16, 32, 8
+    case = workloads.prefill_case(2, (1, 1024), hq, hkv, 128, bs, seed=62, device=DEV, chains=1,
+                                  chain_blocks=2, new_lens=[70, 90], prefix_blocks=[0, 0],
+                                  prefix_chain=[0, 0])
+    # Point both sequences' first two blocks at the same physical blocks and
+    # give them the same keys/values/queries on those 32 positions.
+    bt = case["block_table"].clone()
+    bt[1, :2] = bt[0, :2]
+    q = case["q"].clone()
+    q[70:102] = q[0:32]
+    kn, vn = case["k_new"].clone(), case["v_new"].clone()
+    kn[70:102] = kn[0:32]
+    vn[70:102] = vn[0:32]
+    slots = case["slot_mapping"].clone()
+    slots[70:102] = -1          # the shared rows are stored once, by sequence 0
+    c2 = dict(case, block_table=bt, q=q, k_new=kn, v_new=vn, slot_mapping=slots)
+    gpu_store(c2)
+    out = gpu_prefill(c2)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0:32], out[70:102])
