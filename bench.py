@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+
+One step = one pass of the hot path over one synthetic batch of the
+Qwen3-0.6B-shaped decode workload (256 sequences, context lengths uniform in
+[100, 2048], 16 query / 8 KV heads, head_dim 128, block_size 256, physical
+blocks randomly permuted): pa_store_kvcache of the 256 new tokens, then
+pa_decode. Inputs are resident in HBM before timing starts. The headline
+`value` is algorithmic bytes moved per step / step time (GB/s).
+
+The same JSON line carries:
+  roofline      for pa_decode (split-K attention kernel + its reduce pass),
+                timed with HIP events around each call on the launch stream;
+  cpu_baseline  the CPU oracle (fp64) on the same step, on the host cores;
+  secondary     the other workloads of the pages: Qwen3-8B-shaped decode
+                (512 rows, 41 padding), block-16 stress decode (1024 rows),
+                and Qwen3-8B-shaped varlen prefill with cached prefixes
+                (TFLOP/s against the bf16 MFMA peak).
+Progress goes to stderr; stdout holds only the JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (2.5 PFLOP/s)
+METRIC = "paged decode KV GB/s (% HBM peak); paged prefill TFLOP/s (% MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_slot_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current source of the kernel; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+# ------------------------------------------------------------- byte counts --
+
+def decode_bytes(case):
+    """Algorithmic HBM bytes of one pa_decode call: every K and V row of every
+    context read once, q read for live rows, out written for all rows."""
+    import numpy as np
+    lens = np.asarray(case["lens"], dtype=np.int64)
+    hkv, hq, d = case["num_kv_heads"], case["num_q_heads"], case["head_dim"]
+    kv = int(lens.sum()) * hkv * d * 2 * 2
+    q = int((lens > 0).sum()) * hq * d * 2
+    out = len(lens) * hq * d * 2
+    return kv + q + out
+
+
+def store_bytes(case):
+    """Read k and v of every live new token, write them into the pools."""
+    import torch
+    live = int((case["slot_mapping"] >= 0).sum())
+    return live * case["num_kv_heads"] * case["head_dim"] * 2 * 2 * 2
+
+
+def prefill_flops(case):
+    """4 * Hq * D per causal (query, key) pair: N*P + N(N+1)/2 pairs per sequence."""
+    import numpy as np
+    N = np.asarray(case["new_lens"], dtype=np.int64)
+    P = np.asarray(case["prefix_lens"], dtype=np.int64)
+    pairs = int((N * P + N * (N + 1) // 2).sum())
+    return 4 * case["num_q_heads"] * case["head_dim"] * pairs
+
+
+# ----------------------------------------------------------------- timing --
+
+def run_timed(step, warmup, steps):
+    """Warm up, then time exactly `steps` calls of step(i) between two device
+    synchronisations. Returns (ms per step, [per-step kernel ms])."""
+    import torch
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return ms, [a.elapsed_time(b) for a, b in evs]
+
+
+def decode_bench(cid, warmup, steps):
+    import torch
+    import numpy as np
+    import paged_kv_cache_slot_amd as pa
+    import workloads
+    case = workloads.config_case(cid, device="cuda")
+    B, hq, d = case["q"].shape
+    out = torch.empty_like(case["q"])
+    ws = torch.empty(pa.pa_decode_workspace_bytes(B, hq, d, case["max_context_len"],
+                                                  case["block_size"]),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i, ev):
+        pa.pa_store_kvcache(case["k_new"], case["v_new"], case["k_cache"], case["v_cache"],
+                            case["slot_mapping"])
+        if ev:
+            ev[0].record()
+        pa.pa_decode(out, case["q"], case["k_cache"], case["v_cache"], case["block_table"],
+                     case["context_lens"], case["max_context_len"], case["scale"], ws)
+        if ev:
+            ev[1].record()
+
+    ms, kms = run_timed(step, warmup, steps)
+    dbytes = decode_bytes(case)
+    sbytes = store_bytes(case)
+    kern_ms = float(np.mean(kms))
+    res = dict(case=case, ms_per_step=ms, step_bytes=dbytes + sbytes, decode_bytes=dbytes,
+               decode_ms=kern_ms, gbs=(dbytes + sbytes) / (ms * 1e-3) / 1e9,
+               decode_gbs=dbytes / (kern_ms * 1e-3) / 1e9)
+    return res
+
+
+def prefill_bench(warmup, steps):
+    import torch
+    import numpy as np
+    import paged_kv_cache_slot_amd as pa
+    import workloads
+    case = workloads.config_case(4, device="cuda")
+    out = torch.empty_like(case["q"])
+    torch.cuda.synchronize()
+
+    def step(i, ev):
+        pa.pa_store_kvcache(case["k_new"], case["v_new"], case["k_cache"], case["v_cache"],
+                            case["slot_mapping"])
+        if ev:
+            ev[0].record()
+        pa.pa_prefill_varlen(out, case["q"], case["k_cache"], case["v_cache"],
+                             case["cu_seqlens_q"], case["context_lens"], case["block_table"],
+                             case["max_seqlen_q"], case["scale"])
+        if ev:
+            ev[1].record()
+
+    ms, kms = run_timed(step, warmup, steps)
+    flops = prefill_flops(case)
+    kern_ms = float(np.mean(kms))
+    return dict(ms_per_step=ms, flops=flops, prefill_ms=kern_ms,
+                tflops=flops / (kern_ms * 1e-3) / 1e12, total_q=case["total_q"])
+
+
+def cpu_baseline(case):
+    """The oracle (plain fp64 C++) on the same decode step, on the host cores:
+    the KV store of the new tokens, then attention for every row."""
+    import numpy as np
+    import torch
+    import oracle
+    nthreads = min(oracle.hardware_threads(), len(os.sched_getaffinity(0)), 16)
+    u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    kc, vc = u16(case["k_cache"]), u16(case["v_cache"])
+    kn, vn = u16(case["k_new"]), u16(case["v_new"])
+    slots = case["slot_mapping"].cpu().numpy()
+    bt, cl = case["block_table"].cpu().numpy(), case["context_lens"].cpu().numpy()
+    q = u16(case["q"])
+    t0 = time.perf_counter()
+    oracle.store_kvcache(kn, vn, kc, vc, slots, case["block_size"], inplace=True)
+    oracle.decode(q, kc, vc, bt, cl, case["scale"], nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    nbytes = decode_bytes(case) + store_bytes(case)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole step once: store of {case['batch']} new tokens + fp64 "
+                      f"attention for all {case['batch']} rows x {case['num_q_heads']} heads "
+                      f"(config 2, {int(np.asarray(case['lens']).sum())} context tokens)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (a known "
+                         "byte count for scaling the HBM counters of rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the paged-attention path is built and timed on a "
+              f"single MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_slot_amd as pa
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    pa.library()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB 5 times")
+        return
+    log(f"device: {torch.cuda.get_device_name(0)} "
+        f"({torch.cuda.get_device_properties(0).gcnArchName})")
+
+    log("[bench] config 2: store + decode")
+    main_res = decode_bench(2, args.warmup, args.steps)
+    case = main_res["case"]
+    digest = source_digest("decode.hip", "pa_internal.h")
+    traffic = measured_traffic("pa_decode", digest)
+    roofline = {"kernel": "pa_decode (decode_split_kernel + decode_reduce_kernel)",
+                "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": main_res["decode_bytes"],
+                "avg_launch_us": round(main_res["decode_ms"] * 1e3, 2),
+                "source_digest": digest}
+
+    secondary = []
+    if not args.no_secondary:
+        for cid in (3, 5):
+            log(f"[bench] config {cid}: store + decode")
+            r = decode_bench(cid, args.warmup, args.steps)
+            secondary.append({
+                "workload": workloads.CONFIGS[cid]["name"],
+                "config": cid, "ms_per_step": round(r["ms_per_step"], 4),
+                "step_GBps": round(r["gbs"], 2),
+                "decode_us": round(r["decode_ms"] * 1e3, 2),
+                "decode_GBps": round(r["decode_gbs"], 2),
+                "decode_frac_hbm": round(r["decode_gbs"] / HBM_PEAK_GBS, 4)})
+            del r
+            torch.cuda.empty_cache()
+        log("[bench] config 4: store + prefill")
+        r = prefill_bench(args.warmup, args.steps)
+        secondary.append({
+            "workload": "qwen3_8b_prefill_prefix", "config": 4,
+            "ms_per_step": round(r["ms_per_step"], 4), "prefill_us": round(r["prefill_ms"] * 1e3, 2),
+            "prefill_TFLOPs": round(r["tflops"], 2),
+            "prefill_frac_mfma": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops": r["flops"], "total_q": r["total_q"]})
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(case)
+
+    line = {
+        "metric": METRIC, "value": round(main_res["gbs"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3_0.6b_decode: pa_store_kvcache + pa_decode, 256 sequences, "
+                               "context lengths U[100,2048], 16 q / 8 kv heads, head_dim 128, "
+                               "block_size 256, permuted physical blocks",
+                   "batch": case["batch"], "max_context_len": case["max_context_len"],
+                   "context_tokens": int(sum(case["lens"])), "block_size": case["block_size"],
+                   "num_q_heads": case["num_q_heads"], "num_kv_heads": case["num_kv_heads"],
+                   "head_dim": case["head_dim"], "seed": case["seed"],
+                   "step_bytes": main_res["step_bytes"]},
+        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

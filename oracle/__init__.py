@@ -103,15 +103,21 @@ def hardware_threads(lib=None):
     return int((lib or load()).oracle_hardware_threads())
 
 
-def store_kvcache(k, v, k_cache, v_cache, slot_mapping, block_size, lib=None):
-    """Returns new (k_cache, v_cache) uint16 pools after the store.
+def store_kvcache(k, v, k_cache, v_cache, slot_mapping, block_size, lib=None, inplace=False):
+    """Returns (k_cache, v_cache) uint16 pools after the store.
 
     k, v: [T, Hkv, D] (or [T, >= Hkv*D] rows: the token stride is taken from the
-    array); pools: [num_blocks, block_size, Hkv, D]. The inputs are not changed.
+    array); pools: [num_blocks, block_size, Hkv, D]. The inputs are not changed,
+    unless inplace=True and the pools are C-contiguous uint16 numpy arrays, which
+    are then written in place and returned.
     """
     lib = lib or load()
-    kc = _u16(k_cache).copy()
-    vc = _u16(v_cache).copy()
+    if inplace:
+        kc, vc = k_cache, v_cache
+        assert kc.dtype == np.uint16 and kc.flags.c_contiguous and vc.flags.c_contiguous
+    else:
+        kc = _u16(k_cache).copy()
+        vc = _u16(v_cache).copy()
     num_blocks, bs, hkv, d = kc.shape
     assert bs == block_size
     k, k_stride = _u16_rows(k)
