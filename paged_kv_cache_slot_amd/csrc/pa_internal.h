@@ -90,4 +90,22 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Streaming (non-temporal) 16-byte load and store: data read or written once
+// does not displace reusable lines in the caches, and the memory system keeps
+// a read stream efficient while such writes are interleaved with it.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(void* p, float4 x) {
+  const f32x4_t v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, static_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint4 x) {
+  const u32x4_t v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, static_cast<u32x4_t*>(p));
+}
+
 }  // namespace pa

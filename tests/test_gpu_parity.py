@@ -129,6 +129,26 @@ def test_decode_grid_all_rows(bs, hq, hkv, lens):
             assert int(out[b].float().abs().sum()) == 0
 
 
+def test_decode_more_rows_than_one_scan_window():
+    """2600 rows (more than the 1024 rows of context lengths a work-group holds in
+    LDS at once), mixed lengths and padding: every row against the oracle."""
+    rng = np.random.default_rng(31)
+    lens = rng.integers(1, 700, size=2600)
+    lens[rng.choice(2600, size=150, replace=False)] = 0
+    say("[case] decode 2600 rows, bs=16, Hq=16, Hkv=8, lengths U[1,700) + 150 padding")
+    case = workloads.decode_case(2600, (1, 700), 16, 8, 128, 16, seed=31, device=DEV,
+                                 lens=lens)
+    h = host_copy(case)
+    gpu_store(case)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
+                        nthreads=ORACLE_THREADS)
+    compare(out, ref, "decode 2600 rows")
+    assert int(out[torch.from_numpy(np.flatnonzero(lens == 0)).to(DEV)].float().abs().sum()) == 0
+
+
 def test_decode_max_context_len_above_all_rows():
     """A loose max_context_len (more pieces than any row needs) changes nothing."""
     lens = [40, 300, 0, 513]
