@@ -37,7 +37,8 @@
  *     pa_validate_metadata checks a host copy of it.
  *   - Supported shapes: head_dim == 128; block_size a power of two in
  *     [16, 256]; num_q_heads / num_kv_heads in {1, 2, 4, 8}. bf16 device
- *     buffers must be 16-byte aligned.
+ *     buffers must be 16-byte aligned. The softmax scale of pa_decode and
+ *     pa_prefill_varlen must be positive and finite (else PA_ERR_SHAPE).
  *   - All calls are safe to enqueue from several host threads on different
  *     streams; there is no global state beyond the cached device properties.
  */

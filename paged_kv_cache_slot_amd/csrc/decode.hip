@@ -42,7 +42,6 @@ namespace {
 
 constexpr int kTokensPerRow = kDecodeSplit / 4;  // 64: each 16-lane row takes every 4th token
 constexpr int kScanRows = 1024;                  // rows of context_lens held in LDS at a time
-constexpr int kMaxDevices = 64;
 
 // Merges (m2, l2, acc2) into (m, l, acc): base-2 online-softmax states.
 template <int N>

@@ -1,6 +1,7 @@
 // C ABI of libpa.so: host-side argument checks, then kernel launches on the
 // caller's stream. Nothing here allocates, frees or synchronises. The
 // operations and their sources are documented in include/pa.h.
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -20,6 +21,10 @@ bool supported_group(int32_t hq, int32_t hkv) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// The kernels track each row's maximum raw score, which is the maximum scaled
+// score only for a positive scale.
+bool valid_scale(float scale) { return scale > 0.f && std::isfinite(scale); }
 
 // Checks shared by decode and prefill. Returns PA_OK or the first failure.
 int check_heads(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -89,7 +94,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
               void* stream) {
-  if (batch < 0 || max_context_len < 0 || block_table_stride < 0) return PA_ERR_SHAPE;
+  if (batch < 0 || max_context_len < 0 || block_table_stride < 0 || !valid_scale(scale))
+    return PA_ERR_SHAPE;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
   if (st != PA_OK) return st;
   if (static_cast<int64_t>(block_table_stride) * block_size < max_context_len)
@@ -113,7 +119,8 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void*
                       int32_t total_q, int32_t max_seqlen_q, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                       void* stream) {
-  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || block_table_stride <= 0)
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || block_table_stride <= 0 ||
+      !valid_scale(scale))
     return PA_ERR_SHAPE;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
   if (st != PA_OK) return st;

@@ -16,6 +16,9 @@ constexpr int kHeadDim = 128;
 // handles one (sequence, kv head, piece).
 constexpr int kDecodeSplit = 256;
 
+// Devices whose per-device launch data (occupancy, symbol addresses) is cached.
+constexpr int kMaxDevices = 64;
+
 // ------------------------------------------------------------------ launch --
 
 hipError_t launch_store_kvcache(const uint16_t* k, const uint16_t* v, int64_t kv_token_stride,

@@ -7,25 +7,33 @@
 //
 // Work split. One work-group (4 wavefronts) owns one (sequence, kv head,
 // tile of 128/G new tokens) and all G query heads of that kv head: 128 query
-// rows, 32 per wavefront. It walks the context in tiles of 64 keys.
+// rows, 32 per wavefront. It walks the context in tiles of 64 keys. The
+// work-groups of one (sequence, kv head) pair are all placed on one XCD, back
+// to back, so the pair's K/V stays in that XCD's L2 while they run.
 //
 // Tile pipeline (two LDS stages). Each tile's K and V rows are copied from the
-// pool straight into LDS by global_load_lds (16 bytes per lane, no registers),
-// addressed through the block table (block ids fetched one tile ahead). While
-// tile t is computed, tile t+1 is in flight. Inside a 256-byte row the sixteen
+// pool straight into LDS (buffer/global loads with the LDS-DMA bit, 16 bytes
+// per lane, no registers). A wavefront copies 16 keys, which lie in one cache
+// block, from one scalar base address; keys past the context (a sequence's
+// last tile) re-read token L-1 through per-lane addresses instead. While tile
+// t is computed, tile t+1 is in flight. Inside a 256-byte row the sixteen
 // 16-byte units are stored XOR-swizzled by the key index, so the MFMA operand
 // reads below hit distinct LDS banks.
 //
-// Per wavefront and tile, flash-attention style:
-//   S^T = K Q^T      bf16 MFMA 32x32x16, fp32 accumulate: each lane holds the
-//                    scores of ONE query row, so the row max and sum stay
-//                    in-lane except for one exchange with the lane 32 apart;
-//   p = exp2(s*scale*log2e - m*scale*log2e) with a lazy rescale of the output
-//                    (skipped while no row max of the wavefront moves);
+// Per wavefront and tile, flash-attention style, in log2 units:
+//   Q' = Q * scale * log2(e), rounded to bf16 once per work-group;
+//   S^T = K Q'^T     bf16 MFMA 32x32x16, fp32 accumulate: each lane holds the
+//                    scores of ONE query row, so row reductions stay in-lane
+//                    except for one exchange with the lane 32 apart;
+//   p = 2^(s - mc)   against a per-row reference mc, set from the first
+//                    tile's row maximum and raised (rescaling the output) only
+//                    when a tile's per-lane row sum of p exceeds 256, so no
+//                    per-tile row maximum is needed and p stays <= 256;
 //   O^T += V^T P^T   bf16 MFMA 32x32x16 with P taken straight from the S^T
 //                    accumulators (converted to bf16) and V^T built by
 //                    ds_read_b64_tr_b16 transposed reads from the row-major V
-//                    tile, with keys ordered to match the accumulator layout.
+//                    tile, with keys ordered to match the accumulator layout;
+//                    the row sum adds the same bf16 values (v_dot2 with ones).
 // Tiles wholly above the causal diagonal are skipped per wavefront; tiles
 // wholly below it skip the mask.
 //
@@ -60,12 +68,60 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // transposed V read) all land on distinct units, i.e. distinct LDS banks.
 __device__ __forceinline__ int swz(int key) { return ((key << 1) & 14) | ((key >> 3) & 1); }
 
+// Largest per-lane share of a tile's row sum of exponentials before the row's
+// reference is raised; every exponential stays below it.
+constexpr float kRescaleSum = 256.f;
+constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;  // (1.0, 1.0) in bf16
+
+// v_permlane32_swap of x with itself: the first result holds the low half's
+// values in both halves, the second the high half's, so a symmetric
+// combination of the two gives every lane the combination of itself and the
+// lane 32 apart. (The elements are copied out before the bit casts: a bit cast
+// of a vector element in place reads element 0.)
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t r0 = r[0];
+  const uint32_t r1 = r[1];
+  lo = __builtin_bit_cast(float, r0);
+  hi = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
+}
+
+// Instruction classes of the scheduling-group hint (LLVM AMDGPU).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+// Asks the scheduler for `count` instructions of class `mask` next in the
+// current scheduling region (groups are filled in the order they appear).
+#define sched_group(mask, count) __builtin_amdgcn_sched_group_barrier((mask), (count), 0)
+
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
 
 // 16 bytes per lane from global memory into LDS at dst + 16 * lane.
 __device__ __forceinline__ void dma16(const void* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(dst), 16, 0, 0);
+}
+
+// Raw buffer resource over [base, base + 2^31): scalar base, no stride, no
+// swizzle (dword 3 as for gfx9 raw buffers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+// Same as dma16 from a buffer: lane reads rsrc.base + soff + voff.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff,
+                                          uint16_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(dst), 16, voff, soff, 0, 0);
 }
 
 template <int G>
@@ -115,22 +171,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int col = lane & 31;   // this lane's query row within the wavefront
   const int half = lane >> 5;  // which half of the MFMA k-slices this lane holds
 
-  // This lane's query row; a wavefront's 32 rows are 32 consecutive tokens of
-  // one head (TQ >= 32).
+  // This lane's query row. A wavefront's 32 rows are min(32, TQ) consecutive
+  // tokens of 32 / min(32, TQ) heads.
   const int row = wave * 32 + col;
   const int hh = row / TQ;
   const int tok = row % TQ;
   const int qpos = P + tok0 + tok;                      // absolute position
   const int qt = q0 + min(tok0 + tok, N - 1);           // clamped for loads
   const int head = g * G + hh;
-  const int wave_pos0 = P + tok0 + (wave * 32) % TQ;    // position of the wavefront's first row
+  const int wave_pos0 = P + tok0 + (wave * 32) % TQ;    // lowest position of the wavefront's rows
+  const int wave_pos1 = wave_pos0 + min(32, TQ) - 1;    // highest
 
+  // Q of this lane's row, pre-multiplied by scale * log2(e) and rounded to
+  // bf16 once, so the scores come out of the MFMA in log2 units.
   bf16x8_t qreg[kHeadDim / 16];
   {
     const uint16_t* qp = q + (static_cast<int64_t>(qt) * num_q_heads + head) * kHeadDim + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks)
-      qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + ks * 16);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t sw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sw[i] = pack_bf16x2(bf16_lo(w[i]) * scale_log2, bf16_hi(w[i]) * scale_log2);
+      qreg[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(sw[0], sw[1], sw[2], sw[3]));
+    }
   }
 
   f32x16_t o[kHeadDim / 32];
@@ -138,37 +204,68 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   for (int db = 0; db < kHeadDim / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = -INFINITY;  // running max of this lane's row (raw scores)
-  float lsum = 0.f;     // running sum over this lane's keys
+  // Softmax state of this lane's row, in log2 units: mc is the reference the
+  // exponentials are taken against, p = 2^(s - mc). The score MFMAs start from
+  // -mc (minit), so their output is s - mc directly. mc is set from the first
+  // tile's row maximum and afterwards raised only when a tile's row sum of p
+  // exceeds kRescaleSum, which keeps every p below that bound; the final
+  // o / lsum is the same for any reference.
+  float mc = 0.f;
+  f32x16_t minit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) minit[r] = 0.f;
+  float lsum = 0.f;
 
   const int bs_mask = (1 << log2_bs) - 1;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * bt_stride;
-  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * kHeadDim;
-  const uint16_t* kbase = k_cache + g * kHeadDim;
-  const uint16_t* vbase = v_cache + g * kHeadDim;
+  const int slot_bytes = num_kv_heads * kHeadDim * 2;  // bytes from one slot to the next
 
   // ---- tile loads -----------------------------------------------------------
-  // A tile is 64 keys x 256 B per tensor = 16 global_load_lds instructions of
-  // 1 KiB (4 keys each); wavefront w issues instructions 4w .. 4w+3 for K and
-  // the same for V. Lane l of an instruction carries key (4*instr + l/16) and
-  // the 16-byte unit (l%16) of its LDS row, which holds logical unit
-  // (l%16) ^ swz(key) of the key's 256-byte row. The 4 keys of an instruction
-  // share a block (block_size >= 16), so its block id is one scalar load.
+  // A tile is 64 keys x 256 B per tensor = 16 DMA instructions of 1 KiB (4 keys
+  // each); wavefront w issues instructions 4w .. 4w+3 for K and the same for V,
+  // i.e. keys 16w .. 16w+15 of the tile, which lie in one cache block
+  // (block_size >= 16). Lane l of an instruction carries key (4j + l/16) of
+  // those and the 16-byte unit (l%16) of its LDS row, which holds logical unit
+  // (l%16) ^ swz(key) of the key's 256-byte row.
+  //
+  // Fast path (all 16 keys inside the context): the block's base address is
+  // scalar and each lane adds a fixed 32-bit offset (buffer_load ... lds).
+  // Keys past the context (only in a sequence's last tile) re-read token L-1
+  // instead, with per-lane addresses, so V never holds stale values there.
   const int dma_row = lane >> 4;
   const int dma_unit = lane & 15;
-  auto issue_tile = [&](int t, uint16_t* lk, uint16_t* lv) {
+  uint32_t lane_off[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key0 = (4 * wave + j) * 4;                  // uniform
-      const int kf = min(t * kKeys + key0, L - 1);          // uniform
-      const int blk = bt[kf >> log2_bs];                    // scalar load
-      const int key = key0 + dma_row;
-      const int kc = min(t * kKeys + key, L - 1);  // past the context: re-read token L-1
-      const int64_t off = ((static_cast<int64_t>(blk) << log2_bs) | (kc & bs_mask)) * slot_stride +
-                          ((dma_unit ^ swz(key)) * 8);
-      const int dst = key0 * kHeadDim;  // uniform: 4 rows of 128 elements
-      dma16(kbase + off, lk + dst);
-      dma16(vbase + off, lv + dst);
+  for (int j = 0; j < 4; ++j)
+    lane_off[j] = dma_row * slot_bytes + ((dma_unit ^ swz(4 * j + dma_row)) * 16);
+  const char* kbase = reinterpret_cast<const char*>(k_cache) + g * (kHeadDim * 2);
+  const char* vbase = reinterpret_cast<const char*>(v_cache) + g * (kHeadDim * 2);
+  // Block id of this wavefront's keys in tile t (any valid block past the end).
+  auto block_of = [&](int t) { return bt[min(t * kKeys + 16 * wave, L - 1) >> log2_bs]; };
+  auto issue_tile = [&](int t, int blk, uint16_t* lk, uint16_t* lv) {
+    const int k0 = t * kKeys + 16 * wave;  // first key of this wavefront's 16
+    uint16_t* dk = lk + 16 * wave * kHeadDim;
+    uint16_t* dv = lv + 16 * wave * kHeadDim;
+    if (k0 + 15 < L) {
+      const int64_t first =
+          ((static_cast<int64_t>(blk) << log2_bs) | (k0 & bs_mask)) * slot_bytes;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + first);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + first);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dma16_buf(rk, lane_off[j], j * 4 * slot_bytes, dk + j * 4 * kHeadDim);
+        dma16_buf(rv, lane_off[j], j * 4 * slot_bytes, dv + j * 4 * kHeadDim);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kc = min(k0 + 4 * j + dma_row, L - 1);
+        const int64_t slot =
+            (static_cast<int64_t>(bt[kc >> log2_bs]) << log2_bs) | (kc & bs_mask);
+        const int64_t off = slot * slot_bytes + ((dma_unit ^ swz(4 * j + dma_row)) * 16);
+        dma16(kbase + off, dk + j * 4 * kHeadDim);
+        dma16(vbase + off, dv + j * 4 * kHeadDim);
+      }
     }
   };
 
@@ -192,102 +289,183 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     }
   }
 
-  // ---- pipeline ------------------------------------------------------------
-  // Computes tile t from the LDS stage (kt, vt).
-  auto compute_tile = [&](int t, const uint16_t* kt, uint16_t* vt) {
-      const int kstart = t * kKeys;
-      if (kstart > wave_pos0 + 31) return;       // above the diagonal for every row here
-      const bool full = kstart + kKeys - 1 <= wave_pos0;  // every row sees every key
+  // ---- one tile --------------------------------------------------------------
+  // Computes tile t from the LDS stage (kt, vt); masked selects the causal
+  // mask (diagonal tiles only).
+  auto compute_tile = [&](int t, const uint16_t* kt, uint16_t* vt, bool masked) {
+    // S^T for the two 32-key halves of the tile. The K operands of step ks+2
+    // are read while step ks multiplies.
+    auto read_k = [&](int kb, int ks) {
+      const int key = kb * 32 + col;
+      return *reinterpret_cast<const bf16x8_t*>(kt + key * kHeadDim +
+                                                (((ks * 2 + half) ^ swz(key)) * 8));
+    };
+    // Issue priority: raised while this wavefront feeds the matrix core, so
+    // that the other wavefront on the SIMD runs its softmax in the gaps.
+    __builtin_amdgcn_s_setprio(1);
+    f32x16_t s[2] = {minit, minit};
+    bf16x8_t ka[3][2];
+    ka[0][0] = read_k(0, 0);
+    ka[0][1] = read_k(1, 0);
+    ka[1][0] = read_k(0, 1);
+    ka[1][1] = read_k(1, 1);
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+      if (ks + 2 < kHeadDim / 16) {
+        ka[(ks + 2) % 3][0] = read_k(0, ks + 2);
+        ka[(ks + 2) % 3][1] = read_k(1, ks + 2);
+      }
+      s[0] = mfma32(ka[ks % 3][0], qreg[ks], s[0]);
+      s[1] = mfma32(ka[ks % 3][1], qreg[ks], s[1]);
+    }
+    // Keep that order: two LDS reads in flight ahead of each MFMA pair.
+    sched_group(kSchedDsRead, 4);
+#pragma unroll
+    for (int ks = 0; ks + 2 < kHeadDim / 16; ++ks) {
+      sched_group(kSchedMfma, 2);
+      sched_group(kSchedDsRead, 2);
+    }
+    sched_group(kSchedMfma, 4);
+    __builtin_amdgcn_s_setprio(0);
 
-      // S^T for the two 32-key halves of the tile.
-      f32x16_t s[2];
+    // Mask (lane holds keys kb*32 + (r/4)*8 + half*4 + r%4 of the tile).
+    if (masked) {  // one uniform branch around the whole mask
+      const int rel = qpos - t * kKeys - half * 4;  // key offsets <= rel are visible
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const int key = kb * 32 + col;
-#pragma unroll
-        for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              kt + key * kHeadDim + (((ks * 2 + half) ^ swz(key)) * 8));
-          s[kb] = mfma32(a, qreg[ks], s[kb]);
-        }
-      }
-      // Mask, row max. Lane holds keys kb*32 + (r/4)*8 + half*4 + r%4.
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (!full) {
-            const int kp = kstart + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            s[kb][r] = kp <= qpos ? s[kb][r] : -INFINITY;
-          }
-          tmax = fmaxf(tmax, s[kb][r]);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m, tmax);  // finite: key 0 is visible to every row
-      const float alpha = fast_exp2((m - mn) * scale_log2);
-      m = mn;
-      if (__any(alpha != 1.f)) {  // rescale only when some row max moved
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < kHeadDim / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      const float mc = mn * scale_log2;
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = kb * 32 + (r >> 2) * 8 + (r & 3) <= rel ? s[kb][r] : -INFINITY;
+    }
+    __builtin_amdgcn_s_setprio(1);
 
-      // P (bf16) as the B operand, 16 keys per MFMA step.
-      bf16x8_t pb[4];
+    // P = 2^(s - mc) in bf16 as the B operand, 16 keys per MFMA step; tsum is
+    // this lane's share of the tile's row sum, over the same bf16 values that
+    // enter the product.
+    bf16x8_t pb[4];
+    float tsum;
+    auto make_p = [&]() {
+      float t0 = 0.f, t1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
           uint32_t w[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = fast_exp2(fmaf(s[kb][hs * 8 + 2 * i], scale_log2, -mc));
-            const float p1 = fast_exp2(fmaf(s[kb][hs * 8 + 2 * i + 1], scale_log2, -mc));
-            lsum += p0 + p1;
-            w[i] = pack_bf16x2(p0, p1);
-          }
+          for (int i = 0; i < 4; ++i)
+            w[i] = pack_bf16x2(fast_exp2(s[kb][hs * 8 + 2 * i]),
+                               fast_exp2(s[kb][hs * 8 + 2 * i + 1]));
+          t0 = dot2_bf16(w[0], kOnesBf16x2, t0);
+          t1 = dot2_bf16(w[1], kOnesBf16x2, t1);
+          t0 = dot2_bf16(w[2], kOnesBf16x2, t0);
+          t1 = dot2_bf16(w[3], kOnesBf16x2, t1);
           pb[kb * 2 + hs] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
         }
       }
-      // O^T += V^T P^T.
+      tsum = t0 + t1;
+    };
+    // Moves the reference up to the row maximum where that is higher (to it in
+    // any case on the first tile), rescales the state and recomputes P.
+    auto raise_reference = [&](bool first) {
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int db = 0; db < kHeadDim / 32; ++db) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_ptr)(vt + ks * 16 * kHeadDim + v_off[db][0]));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_ptr)(vt + ks * 16 * kHeadDim + v_off[db][1]));
-          const i16x8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = mfma32(__builtin_bit_cast(bf16x8_t, a8), pb[ks], o[db]);
-        }
-      }
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+      tmax = max_halves(tmax);  // the row's max of s - mc
+      const float d = first ? tmax : fmaxf(tmax, 0.f);
+      const float alpha = first ? 1.f : fast_exp2(-d);  // o and lsum are still 0 on the first
+      mc += d;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < kHeadDim / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= d;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) minit[r] = -mc;
+      make_p();
+    };
+    make_p();
+    // The sum test also catches an overflow to infinity. Per lane: each half
+    // of a row stays below the bound, the row below twice it. The first tile
+    // always sets the reference (one call site keeps register use down).
+    if (t == 0 || __any(!(tsum <= kRescaleSum))) raise_reference(t == 0);
+    lsum += tsum;
+
+    // V^T operands: two transposed reads per (32-row block db, 16-key step ks).
+    auto read_v = [&](int db, int ks, int r) {
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_ptr)(vt + ks * 16 * kHeadDim + v_off[db][r]));
+    };
+    i16x4_t tr[2][4][2];  // two db blocks in flight
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) tr[d][ks][r] = read_v(d, ks, r);
+
+    // O^T += V^T P^T, block db from tr[db % 2]; blocks 2 and 3 are read once
+    // blocks 0 and 1 have been consumed.
+    auto pv = [&](int db, int ks, const i16x4_t (&v)[4][2]) {
+      const i16x8_t a8 = {v[ks][0][0], v[ks][0][1], v[ks][0][2], v[ks][0][3],
+                          v[ks][1][0], v[ks][1][1], v[ks][1][2], v[ks][1][3]};
+      o[db] = mfma32(__builtin_bit_cast(bf16x8_t, a8), pb[ks], o[db]);
+    };
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pv(db, ks, tr[db]);
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) tr[d][ks][r] = read_v(2 + d, ks, r);
+#pragma unroll
+    for (int db = 2; db < 4; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pv(db, ks, tr[db - 2]);
+    // Reads of blocks 2, 3 go between the products of blocks 0, 1.
+    sched_group(kSchedDsRead, 16);
+    sched_group(kSchedMfma, 6);
+    sched_group(kSchedDsRead, 16);
+    sched_group(kSchedMfma, 10);
+    __builtin_amdgcn_s_setprio(0);
   };
-  // One pipeline step: tile t is in (kc, vc); tile t+1 goes into (kn, vn).
+  auto tile = [&](int t, const uint16_t* kt, uint16_t* vt) {
+    const int kstart = t * kKeys;
+    if (kstart > wave_pos1) return;  // above the diagonal for every row here
+    compute_tile(t, kt, vt, kstart + kKeys - 1 > wave_pos0);
+  };
+
+  // ---- pipeline ------------------------------------------------------------
+  // One step: tile t is in (kc, vc); tile t+1 goes into (kn, vn). Block ids
+  // are fetched one step ahead of their DMA.
+  int blk_next = block_of(1);
   auto step = [&](int t, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     // Tile t has landed (this wavefront's copies), then everyone's have, and
     // everyone is done with the stage that tile t+1 will overwrite.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < num_tiles) issue_tile(t + 1, kn, vn);
-    compute_tile(t, kc, vc);
+    if (t + 1 < num_tiles) issue_tile(t + 1, blk_next, kn, vn);
+    tile(t, kc, vc);
+    // Fetched after the tile so that no scalar load is in flight while the
+    // tile's LDS reads are counted (scalar loads return out of order).
+    blk_next = block_of(t + 2);
   };
-  issue_tile(0, lds_k0, lds_v0);
+  issue_tile(0, block_of(0), lds_k0, lds_v0);
   for (int t = 0; t < num_tiles; t += 2) {
     step(t, lds_k0, lds_v0, lds_k1, lds_v1);
     if (t + 1 < num_tiles) step(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
   }
 
   // Normalise and write. Lane holds d = db*32 + (r/4)*8 + half*4 + r%4.
-  lsum += __shfl_xor(lsum, 32);
-  const float inv = 1.f / lsum;
+  const float inv = 1.f / sum_halves(lsum);
   if (tok0 + tok < N) {
     uint16_t* op = out + (static_cast<int64_t>(q0 + tok0 + tok) * num_q_heads + head) * kHeadDim;
 #pragma unroll

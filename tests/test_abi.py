@@ -87,6 +87,8 @@ def test_decode_argument_checks(lib):
     assert call(wsb=ws - 1) == PA_ERR_WORKSPACE
     assert call(ws=None) == PA_ERR_WORKSPACE
     assert call(maxl=-1) == PA_ERR_SHAPE
+    for bad in (0.0, -0.088, float("nan"), float("inf")):
+        assert call(scale=bad) == PA_ERR_SHAPE
 
 
 def test_prefill_argument_checks(lib):
@@ -97,6 +99,8 @@ def test_prefill_argument_checks(lib):
     assert f(P, P, P, P, P, P, P, 4, 2, 10, 8, 32, 8, 96, 256, 0.1, None) == PA_ERR_UNSUPPORTED
     assert f(P, P, P, P, P, P, P, 4, 2, 10, 8, 30, 8, 128, 256, 0.1, None) == PA_ERR_SHAPE
     assert f(P, P, P, P, P, P, P, 0, 2, 10, 8, 32, 8, 128, 256, 0.1, None) == PA_ERR_SHAPE
+    for bad in (0.0, -0.1, float("nan"), float("inf")):
+        assert f(P, P, P, P, P, P, P, 4, 2, 10, 8, 32, 8, 128, 256, bad, None) == PA_ERR_SHAPE
 
 
 def test_workspace_size():
