@@ -62,11 +62,19 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N],
 // s_pref[i] = `base` + the number of pieces of rows start .. start+i-1,
 // s_pref[n] = base + all of them. A padding row (length 0) counts as one piece,
 // which writes its zeros.
+// Orders the LDS accesses of one wavefront (the wavefronts of a work-group
+// run independently, so a work-group barrier must not be used).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ int scan_rows(const int32_t* __restrict__ context_lens, int start, int batch,
                          int max_context_len, int base, int* s_pref, int* s_len) {
   constexpr int kPer = kScanRows / 64;
   const int n = min(kScanRows, batch - start);
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   int raw[kPer];  // all loads first (index clamped), so they share one round trip
 #pragma unroll
   for (int r = 0; r < kPer; ++r) raw[r] = context_lens[start + min(lane * kPer + r, n - 1)];
@@ -98,7 +106,7 @@ __device__ int scan_rows(const int32_t* __restrict__ context_lens, int start, in
     excl += cnt[r];
   }
   if (lane == 63) s_pref[n] = excl;
-  __syncthreads();
+  wave_sync();
   return n;
 }
 
@@ -109,8 +117,13 @@ struct Item {
   int valid, b, g, split, L, nsplit;
 };
 
+// Wavefronts per work-group: all that fit on a CU at once (two per SIMD, one
+// for G = 8, whose register use allows only one).
+template <int G>
+constexpr int decode_waves() { return G >= 8 ? 4 : 8; }
+
 template <int G, int CH>
-__global__ __launch_bounds__(64, G >= 8 ? 1 : 2) void decode_kernel(
+__global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int32_t bt_stride,
@@ -122,10 +135,17 @@ __global__ __launch_bounds__(64, G >= 8 ? 1 : 2) void decode_kernel(
   // the stand-in back into a branch).
   constexpr int NCH = kTokensPerRow / CH;  // chunks per piece
   static_assert(NCH % 2 == 0, "chunk buffers alternate, so a piece has an even chunk count");
-  __shared__ int s_pref[kScanRows + 1];
-  __shared__ int s_len[kScanRows];
+  constexpr int W = decode_waves<G>();
+  __shared__ int s_pref_all[W][kScanRows + 1];  // each wavefront's window of context_lens
+  __shared__ int s_len_all[W][kScanRows];
+  __shared__ int s_taken;                       // items of this work-group handed out so far
+  if (threadIdx.x == 0) s_taken = 0;
+  __syncthreads();  // the only work-group barrier: every wavefront is here once, at the start
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int* s_pref = s_pref_all[wave];
+  int* s_len = s_len_all[wave];
   const int grp = lane >> 4;  // which token of four
   const int sub = lane & 15;  // which 8-element slice of head_dim
   const int bs_mask = (1 << log2_bs) - 1;
@@ -144,7 +164,7 @@ __global__ __launch_bounds__(64, G >= 8 ? 1 : 2) void decode_kernel(
     while (p >= __builtin_amdgcn_readfirstlane(s_pref[nrows])) {
       if (chunk_start + nrows >= batch) return fallback;  // past the last item
       const int base = __builtin_amdgcn_readfirstlane(s_pref[nrows]);
-      __syncthreads();
+      wave_sync();
       chunk_start += nrows;
       nrows = scan_rows(context_lens, chunk_start, batch, max_context_len, base, s_pref, s_len);
     }
@@ -337,15 +357,20 @@ __global__ __launch_bounds__(64, G >= 8 ? 1 : 2) void decode_kernel(
   // slot of the finished item is then refilled with the item after that. The
   // loop body is unrolled over the two slots so that no register holding an
   // in-flight load is ever copied (a copy would wait for the load).
-  int w = blockIdx.x;
-  Item ia = lookup(w, Item{0, 0, 0, 0, 0, 0});
-  if (!ia.valid) return;
+  //
+  // Work-group i owns items i, i + grid, i + 2 grid, ...: its k-th item is
+  // k * grid + i. Wavefront j takes its k = j and k = W + j first; every later
+  // k comes from the work-group's LDS counter, fetched when the item two
+  // places before it starts, so wavefronts that run faster take more items.
+  auto item_index = [&](int k) { return k * static_cast<int>(gridDim.x) + blockIdx.x; };
+  Item ia = lookup(item_index(wave), Item{0, 0, 0, 0, 0, 0});
+  if (ia.valid) {
   int blk_a = load_blocks(ia);
   uint32_t q_a[G][4], q_b[G][4];
   load_q(ia, q_a);
   uint4 kr0[CH], vr0[CH], kr1[CH], vr1[CH];
   issue(ia, blk_a, 0, kr0, vr0);
-  Item ib = lookup(w + gridDim.x, ia);
+  Item ib = lookup(item_index(W + wave), ia);
   int blk_b = load_blocks(ib);
   load_q(ib, q_b);
 
@@ -354,6 +379,8 @@ __global__ __launch_bounds__(64, G >= 8 ? 1 : 2) void decode_kernel(
   // false when `nxt` does not exist.
   auto run = [&](Item& cur, int& cur_blk, uint32_t (&qc)[G][4], const Item& nxt, int nxt_blk)
       -> bool {
+    int grabbed = 0;  // lane 0: k - 2W of the item that will refill this slot
+    if (lane == 0) grabbed = atomicAdd(&s_taken, 1);
     reset();
     const int t0 = cur.split * kDecodeSplit;
     const int ntok = min(cur.L, t0 + kDecodeSplit) - t0;  // <= 0 on a padding row
@@ -369,8 +396,7 @@ __global__ __launch_bounds__(64, G >= 8 ? 1 : 2) void decode_kernel(
     }
     finalize(cur);
     if (!nxt.valid) return false;
-    w += gridDim.x;
-    cur = lookup(w + gridDim.x, nxt);
+    cur = lookup(item_index(2 * W + __builtin_amdgcn_readfirstlane(grabbed)), nxt);
     cur_blk = load_blocks(cur);
     load_q(cur, qc);
     return true;
@@ -378,6 +404,7 @@ __global__ __launch_bounds__(64, G >= 8 ? 1 : 2) void decode_kernel(
   for (;;) {
     if (!run(ia, blk_a, q_a, ib, blk_b)) break;
     if (!run(ib, blk_b, q_b, ia, blk_a)) break;
+  }
   }
 }
 
@@ -419,7 +446,8 @@ int resident_groups() {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<G, CH>, 64, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<G, CH>,
+                                                   64 * decode_waves<G>(), 0) !=
           hipSuccess || per_cu <= 0)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -431,19 +459,21 @@ int resident_groups() {
 }
 
 template <int G, int CH>
-void launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+hipError_t launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                   const uint16_t* v_cache, const int32_t* block_table, int32_t bt_stride,
                   const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                   int32_t num_kv_heads, int32_t log2_bs, int32_t max_context_len,
                   float scale_log2, int32_t max_splits, float* ws_o, float* ws_ml,
                   hipStream_t stream) {
-  // Never more work-groups than items (pieces x kv heads).
+  // Never more wavefronts than items (pieces x kv heads).
   const int64_t items = static_cast<int64_t>(batch) * num_kv_heads * max_splits;
-  const int64_t blocks = std::min<int64_t>(items, resident_groups<G, CH>());
-  hipLaunchKernelGGL((decode_kernel<G, CH>), dim3(static_cast<uint32_t>(blocks)), dim3(64), 0,
-                     stream, out, q, k_cache, v_cache, block_table, bt_stride, context_lens,
-                     batch, num_q_heads, num_kv_heads, log2_bs, max_context_len, scale_log2,
-                     max_splits, ws_o, ws_ml, 0);
+  constexpr int W = decode_waves<G>();
+  const int64_t blocks = std::min<int64_t>((items + W - 1) / W, resident_groups<G, CH>());
+  hipLaunchKernelGGL((decode_kernel<G, CH>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * decode_waves<G>()), 0, stream, out, q, k_cache, v_cache,
+                     block_table, bt_stride, context_lens, batch, num_q_heads, num_kv_heads,
+                     log2_bs, max_context_len, scale_log2, max_splits, ws_o, ws_ml, 0);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -466,11 +496,13 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   const int log2_bs = __builtin_ctz(static_cast<unsigned>(block_size));
   const float scale_log2 = scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
+  hipError_t err = hipSuccess;
 #define PA_DECODE_CASE(GG, CC)                                                              \
   case GG:                                                                                 \
-    launch_split<GG, CC>(out, q, k_cache, v_cache, block_table, block_table_stride,        \
-                         context_lens, batch, num_q_heads, num_kv_heads, log2_bs,          \
-                         max_context_len, scale_log2, max_splits, ws_o, ws_ml, stream);    \
+    err = launch_split<GG, CC>(out, q, k_cache, v_cache, block_table, block_table_stride,  \
+                               context_lens, batch, num_q_heads, num_kv_heads, log2_bs,    \
+                               max_context_len, scale_log2, max_splits, ws_o, ws_ml,       \
+                               stream);                                                    \
     break;
   switch (G) {
     PA_DECODE_CASE(1, 8)
@@ -481,7 +513,6 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
       return hipErrorInvalidValue;
   }
 #undef PA_DECODE_CASE
-  hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (max_splits > 1) {
     hipLaunchKernelGGL(decode_reduce_kernel,
