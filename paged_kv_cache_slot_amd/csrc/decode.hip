@@ -40,8 +40,9 @@
 namespace pa {
 namespace {
 
-constexpr int kTokensPerRow = kDecodeSplit / 4;  // 64: each 16-lane row takes every 4th token
-constexpr int kScanRows = 1024;                  // rows of context_lens held in LDS at a time
+constexpr int kScanRows = 1024;        // rows of context_lens held in LDS at a time
+constexpr int kMaxGroupItems = 4096;   // items one work-group can own (LDS table)
+constexpr int kSizeClasses = 16;       // item-size classes of the largest-first order
 
 // Merges (m2, l2, acc2) into (m, l, acc): base-2 online-softmax states.
 template <int N>
@@ -62,54 +63,6 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N],
 // s_pref[i] = `base` + the number of pieces of rows start .. start+i-1,
 // s_pref[n] = base + all of them. A padding row (length 0) counts as one piece,
 // which writes its zeros.
-// Orders the LDS accesses of one wavefront (the wavefronts of a work-group
-// run independently, so a work-group barrier must not be used).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ int scan_rows(const int32_t* __restrict__ context_lens, int start, int batch,
-                         int max_context_len, int base, int* s_pref, int* s_len) {
-  constexpr int kPer = kScanRows / 64;
-  const int n = min(kScanRows, batch - start);
-  const int lane = threadIdx.x & 63;
-  int raw[kPer];  // all loads first (index clamped), so they share one round trip
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) raw[r] = context_lens[start + min(lane * kPer + r, n - 1)];
-  int cnt[kPer];
-  int local = 0;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = lane * kPer + r;
-    int c = 0;
-    if (i < n) {
-      const int L = max(0, min(raw[r], max_context_len));
-      s_len[i] = L;
-      c = max(1, (L + kDecodeSplit - 1) / kDecodeSplit);
-    }
-    cnt[r] = c;
-    local += c;
-  }
-  int incl = local;  // inclusive scan over the 64 lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  int excl = base + incl - local;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = lane * kPer + r;
-    if (i < n) s_pref[i] = excl;
-    excl += cnt[r];
-  }
-  if (lane == 63) s_pref[n] = excl;
-  wave_sync();
-  return n;
-}
-
 // One work item: piece `split` (tokens [split*256, min(L, split*256+256))) of
 // sequence b, kv head g. L is the clamped context length (0: padding row) and
 // nsplit the sequence's number of pieces. All fields are uniform.
@@ -129,57 +82,171 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
     const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ context_lens, int32_t batch, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t log2_bs, int32_t max_context_len, float scale_log2,
-    int32_t max_splits, float* __restrict__ ws_o, float* __restrict__ ws_ml, int32_t zero) {
+    int32_t max_splits, int32_t log2_split, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    int32_t zero) {
   // `zero` is always 0. Adding it to the address of a stand-in load keeps the
   // compiler from merging that load with an identical one (and from turning
   // the stand-in back into a branch).
-  constexpr int NCH = kTokensPerRow / CH;  // chunks per piece
-  static_assert(NCH % 2 == 0, "chunk buffers alternate, so a piece has an even chunk count");
   constexpr int W = decode_waves<G>();
-  __shared__ int s_pref_all[W][kScanRows + 1];  // each wavefront's window of context_lens
-  __shared__ int s_len_all[W][kScanRows];
-  __shared__ int s_taken;                       // items of this work-group handed out so far
-  if (threadIdx.x == 0) s_taken = 0;
-  __syncthreads();  // the only work-group barrier: every wavefront is here once, at the start
+  constexpr int kThreads = 64 * W;
+  const int split = 1 << log2_split;  // tokens per piece
+  __shared__ int s_pref[kScanRows + 1];         // full pieces before each sequence
+  __shared__ int s_len[kScanRows];              // clamped lengths
+  __shared__ int4 s_items[kMaxGroupItems];      // this work-group's items: (b, piece, L, g)
+  __shared__ int s_order[kMaxGroupItems];       // item indices, largest first
+  __shared__ int s_class[kSizeClasses];         // per size class: count, then next slot
+  __shared__ int s_misc[4];                     // [1] items handed out, [2] items owned
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int* s_pref = s_pref_all[wave];
-  int* s_len = s_len_all[wave];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4;  // which token of four
   const int sub = lane & 15;  // which 8-element slice of head_dim
   const int bs_mask = (1 << log2_bs) - 1;
   const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * kHeadDim;
 
   // ---- the item list -------------------------------------------------------
-  int chunk_start = 0;
-  int nrows = scan_rows(context_lens, 0, batch, max_context_len, 0, s_pref, s_len);
-  // Item w (may rescan the LDS window). Past the last item it returns
+  // A launch covers at most kScanRows sequences (larger batches go in slices).
+  // Sequence b has nfull_b = L_b / split full pieces and, when L_b is not a
+  // multiple of split, one partial piece of r_b tokens (a padding row, L = 0,
+  // has one item that writes its zeros). An item is (piece, kv head); its cost
+  // is its number of 32-token chunks plus one. In the global order all full
+  // items come first, in (sequence, piece, kv head) order, then the partial
+  // ones in (sequence, kv head) order. Work-group i takes the items whose first
+  // cost unit falls in its share [i C / grid, (i+1) C / grid) of the total C,
+  // so all work-groups get the same cost to within one item; it keeps them in
+  // LDS, largest first (full pieces, then partial pieces by size), so the small
+  // ones come last and the wavefronts finish together.
+  const int grid = static_cast<int>(gridDim.x);
+  const int hkv = num_kv_heads;
+  const int full_cost = (split >> 5) + 1;
+  auto part_cost = [](int r) { return ((r + 31) >> 5) + 1; };  // r tokens, r < split
+  constexpr int kPer = (kScanRows + kThreads - 1) / kThreads;  // sequences per thread
+  int nfull[kPer], pcost[kPer];
+  int fsum = 0, psum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int b = tid * kPer + j;
+    int nf = 0, pc = 0;
+    if (b < batch) {
+      const int L = max(0, min(context_lens[b], max_context_len));
+      s_len[b] = L;
+      nf = L >> log2_split;
+      const int r = L - (nf << log2_split);
+      pc = (r > 0 || L == 0) ? part_cost(r) : 0;
+    }
+    nfull[j] = nf;
+    pcost[j] = pc;
+    fsum += nf;
+    psum += pc;
+  }
+  // Exclusive scans of full pieces and partial costs over the sequences.
+  int fincl = fsum, pincl = psum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int fv = __shfl_up(fincl, off), pv = __shfl_up(pincl, off);
+    if (lane >= off) {
+      fincl += fv;
+      pincl += pv;
+    }
+  }
+  if (lane == 63) {
+    s_pref[wave] = fincl;       // per-wavefront totals (s_pref reused as scratch)
+    s_pref[W + wave] = pincl;
+  }
+  if (tid < kSizeClasses) s_class[tid] = 0;
+  if (tid == 0) s_misc[2] = 0;
+  __syncthreads();
+  int fbase = fincl - fsum, pbase = pincl - psum, ftot = 0, ptot = 0;
+  for (int w2 = 0; w2 < W; ++w2) {
+    const int fw = s_pref[w2], pw = s_pref[W + w2];
+    if (w2 < wave) {
+      fbase += fw;
+      pbase += pw;
+    }
+    ftot += fw;
+    ptot += pw;
+  }
+  __syncthreads();  // s_pref is rewritten below
+  int* s_fpre = s_pref;  // full pieces before sequence b (s_fpre[batch] = all)
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int b = tid * kPer + j;
+    if (b < batch) s_fpre[b] = fbase;
+    fbase += nfull[j];
+  }
+  if (tid == 0) s_fpre[batch] = ftot;
+  __syncthreads();
+  const int64_t full_items = static_cast<int64_t>(ftot) * hkv;
+  const int64_t total = full_items * full_cost + static_cast<int64_t>(ptot) * hkv;
+  const int64_t lo = total * blockIdx.x / grid, hi = total * (blockIdx.x + 1) / grid;
+  auto add_item = [&](int b, int piece, int g) {
+    const int slot = atomicAdd(&s_misc[2], 1);
+    if (slot < kMaxGroupItems) s_items[slot] = make_int4(b, piece, s_len[b], g);
+  };
+  // Full items f whose first unit f * full_cost is in [lo, hi).
+  const int64_t f0 = std::min<int64_t>(full_items, (lo + full_cost - 1) / full_cost);
+  const int64_t f1 = std::min<int64_t>(full_items, (hi + full_cost - 1) / full_cost);
+  for (int64_t f = f0 + tid; f < f1; f += kThreads) {
+    const int pg = static_cast<int>(f / hkv);  // global full piece
+    int blo = 0, bhi = batch - 1;             // sequence b with s_fpre[b] <= pg < s_fpre[b+1]
+    while (blo < bhi) {
+      const int mid = (blo + bhi + 1) >> 1;
+      if (s_fpre[mid] <= pg) blo = mid; else bhi = mid - 1;
+    }
+    add_item(blo, pg - s_fpre[blo], static_cast<int>(f - static_cast<int64_t>(pg) * hkv));
+  }
+  // Partial items: (b, g) starts at full_items * full_cost + hkv * pbase_b + g * pcost_b.
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int b = tid * kPer + j;
+    const int pb0 = pbase;
+    pbase += pcost[j];
+    if (b >= batch || pcost[j] == 0) continue;
+    for (int g = 0; g < hkv; ++g) {
+      const int64_t st = full_items * full_cost + static_cast<int64_t>(hkv) * pb0 +
+                         static_cast<int64_t>(g) * pcost[j];
+      if (st >= lo && st < hi) add_item(b, nfull[j], g);
+    }
+  }
+  __syncthreads();
+  const int nitems = min(kMaxGroupItems, s_misc[2]);
+  // Largest first: a counting sort over size classes (class kSizeClasses-1
+  // holds the full pieces and the padding rows).
+  auto size_class = [&](int4 it) {
+    const int tokens = it.z > 0 ? min(split, it.z - it.y * split) : split;
+    return min(kSizeClasses - 1, (tokens * kSizeClasses - 1) >> log2_split);
+  };
+  for (int k = tid; k < nitems; k += kThreads) atomicAdd(&s_class[size_class(s_items[k])], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int c = kSizeClasses - 1; c >= 0; --c) {
+      const int cnt = s_class[c];
+      s_class[c] = acc;
+      acc += cnt;
+    }
+    s_misc[1] = 0;
+  }
+  __syncthreads();
+  for (int k = tid; k < nitems; k += kThreads)
+    s_order[atomicAdd(&s_class[size_class(s_items[k])], 1)] = k;
+  __syncthreads();  // the last work-group barrier: from here on wavefronts run independently
+
+  // The rank-th item (largest first). Past the last item it returns
   // `fallback` marked invalid, so that the loads issued for it still read
   // valid memory.
-  auto lookup = [&](int w, Item fallback) -> Item {
+  auto lookup = [&](int rank, Item fallback) -> Item {
     fallback.valid = 0;
-    Item it = fallback;
-    const int p = w / num_kv_heads;
-    while (p >= __builtin_amdgcn_readfirstlane(s_pref[nrows])) {
-      if (chunk_start + nrows >= batch) return fallback;  // past the last item
-      const int base = __builtin_amdgcn_readfirstlane(s_pref[nrows]);
-      wave_sync();
-      chunk_start += nrows;
-      nrows = scan_rows(context_lens, chunk_start, batch, max_context_len, base, s_pref, s_len);
-    }
-    int lo = 0, hi = nrows - 1;  // row r with s_pref[r] <= p < s_pref[r + 1]
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= p) lo = mid; else hi = mid - 1;
-    }
-    const int first = __builtin_amdgcn_readfirstlane(s_pref[lo]);
+    if (rank >= nitems) return fallback;
+    const int4 e = s_items[__builtin_amdgcn_readfirstlane(s_order[rank])];
+    Item it;
     it.valid = 1;
-    it.b = chunk_start + lo;
-    it.g = w - p * num_kv_heads;
-    it.split = p - first;
-    it.nsplit = __builtin_amdgcn_readfirstlane(s_pref[lo + 1]) - first;
-    it.L = __builtin_amdgcn_readfirstlane(s_len[lo]);
+    it.b = __builtin_amdgcn_readfirstlane(e.x);
+    it.split = __builtin_amdgcn_readfirstlane(e.y);
+    it.L = __builtin_amdgcn_readfirstlane(e.z);
+    it.g = __builtin_amdgcn_readfirstlane(e.w);
+    it.nsplit = max(1, (it.L + split - 1) >> log2_split);
     return it;
   };
   // Every path issues the same vector loads in the same order (a load that is
@@ -190,13 +257,13 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
     return q + (static_cast<int64_t>(it.b) * num_q_heads + it.g * G) * kHeadDim + sub * 8;
   };
   // The item's block ids: lane l holds the block-table entry (first block of
-  // the piece) + l % 16, clamped into the row (entries past the context are
-  // never used). A piece of 256 tokens spans at most 16 blocks because
-  // block_size >= 16, and each group of 4 tokens lies in one block.
+  // the piece) + l, clamped into the row (entries past the context are never
+  // used). A piece spans at most 64 blocks (the host keeps the piece size at
+  // or below 64 blocks), and each group of 4 tokens lies in one block.
   auto load_blocks = [&](const Item& it) -> int {
-    const int bidx0 = (it.split * kDecodeSplit) >> log2_bs;
+    const int bidx0 = (it.split << log2_split) >> log2_bs;
     const int32_t* src = it.L > 0 ? block_table + static_cast<int64_t>(it.b) * bt_stride +
-                                        min(bidx0 + (lane & 15), bt_stride - 1)
+                                        min(bidx0 + lane, bt_stride - 1)
                                   : reinterpret_cast<const int32_t*>(q_row(it) + zero);
     return *src;
   };
@@ -215,7 +282,7 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   // inside the last group re-read token L-1 of the same block, and a chunk with
   // no tokens at all reads the item's q row.
   auto issue = [&](const Item& it, int my_blk, int c, uint4 (&kb)[CH], uint4 (&vb)[CH]) {
-    const int t0 = it.split * kDecodeSplit;
+    const int t0 = it.split << log2_split;
     const int cbase = t0 + c * CH * 4;
     const bool active = cbase < it.L;  // uniform
     const int bidx0 = t0 >> log2_bs;
@@ -259,7 +326,7 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   };
   auto compute = [&](const Item& it, int c, const uint32_t (&qv)[G][4], const uint4 (&kb)[CH],
                      const uint4 (&vb)[CH]) {
-    const int cbase = it.split * kDecodeSplit + c * CH * 4;
+    const int cbase = (it.split << log2_split) + c * CH * 4;
     if (cbase >= it.L) return;  // uniform
     float s[CH][G];
 #pragma unroll
@@ -358,19 +425,17 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   // loop body is unrolled over the two slots so that no register holding an
   // in-flight load is ever copied (a copy would wait for the load).
   //
-  // Work-group i owns items i, i + grid, i + 2 grid, ...: its k-th item is
-  // k * grid + i. Wavefront j takes its k = j and k = W + j first; every later
-  // k comes from the work-group's LDS counter, fetched when the item two
-  // places before it starts, so wavefronts that run faster take more items.
-  auto item_index = [&](int k) { return k * static_cast<int>(gridDim.x) + blockIdx.x; };
-  Item ia = lookup(item_index(wave), Item{0, 0, 0, 0, 0, 0});
+  // Wavefront j takes the work-group's items of rank j and W + j first; every
+  // later rank comes from the work-group's LDS counter, fetched when the item
+  // two places before it starts, so wavefronts that run faster take more.
+  Item ia = lookup(wave, Item{0, 0, 0, 0, 0, 0});
   if (ia.valid) {
   int blk_a = load_blocks(ia);
   uint32_t q_a[G][4], q_b[G][4];
   load_q(ia, q_a);
   uint4 kr0[CH], vr0[CH], kr1[CH], vr1[CH];
   issue(ia, blk_a, 0, kr0, vr0);
-  Item ib = lookup(item_index(W + wave), ia);
+  Item ib = lookup(W + wave, ia);
   int blk_b = load_blocks(ib);
   load_q(ib, q_b);
 
@@ -379,11 +444,11 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   // false when `nxt` does not exist.
   auto run = [&](Item& cur, int& cur_blk, uint32_t (&qc)[G][4], const Item& nxt, int nxt_blk)
       -> bool {
-    int grabbed = 0;  // lane 0: k - 2W of the item that will refill this slot
-    if (lane == 0) grabbed = atomicAdd(&s_taken, 1);
+    int grabbed = 0;  // lane 0: rank - 2W of the item that will refill this slot
+    if (lane == 0) grabbed = atomicAdd(&s_misc[1], 1);
     reset();
-    const int t0 = cur.split * kDecodeSplit;
-    const int ntok = min(cur.L, t0 + kDecodeSplit) - t0;  // <= 0 on a padding row
+    const int t0 = cur.split << log2_split;
+    const int ntok = min(cur.L, t0 + split) - t0;  // <= 0 on a padding row
     const int nch = max(0, (ntok + 4 * CH - 1) / (4 * CH));
     for (int c = 0;; c += 2) {
       issue(cur, cur_blk, c + 1, kr1, vr1);
@@ -396,7 +461,7 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
     }
     finalize(cur);
     if (!nxt.valid) return false;
-    cur = lookup(item_index(2 * W + __builtin_amdgcn_readfirstlane(grabbed)), nxt);
+    cur = lookup(2 * W + __builtin_amdgcn_readfirstlane(grabbed), nxt);
     cur_blk = load_blocks(cur);
     load_q(cur, qc);
     return true;
@@ -412,12 +477,12 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
 // (sequence, query head), one thread per element of head_dim.
 __global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(
     uint16_t* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t num_q_heads,
-    int32_t max_context_len, int32_t max_splits, const float* __restrict__ ws_o,
-    const float* __restrict__ ws_ml) {
+    int32_t max_context_len, int32_t max_splits, int32_t log2_split,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_ml) {
   const int64_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / num_q_heads);
   const int L = min(context_lens[b], max_context_len);
-  const int nsplit = min((L + kDecodeSplit - 1) / kDecodeSplit, max_splits);
+  const int nsplit = min((L + (1 << log2_split) - 1) >> log2_split, max_splits);
   if (nsplit <= 1) return;  // written by the split kernel (or a padding row)
   const int d = threadIdx.x;
   const float* ml = ws_ml + bh * max_splits * 2;
@@ -432,8 +497,9 @@ __global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(
   out[bh * kHeadDim + d] = static_cast<uint16_t>(pack_bf16x2(o / lt, 0.f) & 0xffffu);
 }
 
-int max_splits_for(int32_t max_context_len) {
-  return max(1, (max_context_len + kDecodeSplit - 1) / kDecodeSplit);
+// Pieces per context of max_context_len tokens, for pieces of 2^log2_split.
+int max_splits_for(int32_t max_context_len, int log2_split) {
+  return max(1, (max_context_len + (1 << log2_split) - 1) >> log2_split);
 }
 
 // Work-groups of decode_kernel<G, CH> resident at once on the current device
@@ -458,28 +524,59 @@ int resident_groups() {
   return v;
 }
 
+// One launch of the split kernel (and the reduce, if needed) over the first
+// sequences of `batch`: at most kScanRows of them, and few enough that no
+// work-group can own more than kMaxGroupItems items (a work-group's share of
+// the cost, over the cheapest item's cost). Pieces are 512 tokens, or 64
+// blocks if that is less. Returns the number of sequences handled (the caller
+// goes on with the rest).
 template <int G, int CH>
-hipError_t launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
-                  const uint16_t* v_cache, const int32_t* block_table, int32_t bt_stride,
-                  const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-                  int32_t num_kv_heads, int32_t log2_bs, int32_t max_context_len,
-                  float scale_log2, int32_t max_splits, float* ws_o, float* ws_ml,
-                  hipStream_t stream) {
-  // Never more wavefronts than items (pieces x kv heads).
-  const int64_t items = static_cast<int64_t>(batch) * num_kv_heads * max_splits;
+int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                 const uint16_t* v_cache, const int32_t* block_table, int32_t bt_stride,
+                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t log2_bs, int32_t max_context_len, float scale_log2,
+                 float* workspace, hipStream_t stream, hipError_t* err) {
   constexpr int W = decode_waves<G>();
-  const int64_t blocks = std::min<int64_t>((items + W - 1) / W, resident_groups<G, CH>());
-  hipLaunchKernelGGL((decode_kernel<G, CH>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(64 * decode_waves<G>()), 0, stream, out, q, k_cache, v_cache,
-                     block_table, bt_stride, context_lens, batch, num_q_heads, num_kv_heads,
-                     log2_bs, max_context_len, scale_log2, max_splits, ws_o, ws_ml, 0);
-  return hipGetLastError();
+  const int groups = resident_groups<G, CH>();
+  const int log2_split = std::min(9, log2_bs + 6);
+  const int64_t per_seq = static_cast<int64_t>(num_kv_heads) *
+                          max_splits_for(max_context_len, log2_split) *
+                          ((1 << (log2_split - 5)) + 1);  // items x highest item cost
+  const int64_t nb_max = static_cast<int64_t>(kMaxGroupItems - 4) * groups / per_seq;
+  const int nb = static_cast<int>(std::min<int64_t>({batch, kScanRows, nb_max}));
+  if (nb <= 0) {
+    *err = hipErrorInvalidValue;
+    return 0;
+  }
+  auto items_for = [&](int lg, int64_t n) {
+    return n * num_kv_heads * max_splits_for(max_context_len, lg);
+  };
+  const int max_splits = max_splits_for(max_context_len, log2_split);
+  float* ws_o = workspace;
+  float* ws_ml = ws_o + static_cast<size_t>(nb) * num_q_heads * max_splits * kHeadDim;
+  // Never more wavefronts than items.
+  const int64_t blocks = std::min<int64_t>((items_for(log2_split, nb) + W - 1) / W, groups);
+  hipLaunchKernelGGL((decode_kernel<G, CH>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * W),
+                     0, stream, out, q, k_cache, v_cache, block_table, bt_stride, context_lens,
+                     nb, num_q_heads, num_kv_heads, log2_bs, max_context_len, scale_log2,
+                     max_splits, log2_split, ws_o, ws_ml, 0);
+  *err = hipGetLastError();
+  if (*err == hipSuccess && max_splits > 1) {
+    hipLaunchKernelGGL(decode_reduce_kernel,
+                       dim3(static_cast<uint32_t>(static_cast<int64_t>(nb) * num_q_heads)),
+                       dim3(kHeadDim), 0, stream, out, context_lens, num_q_heads,
+                       max_context_len, max_splits, log2_split, ws_o, ws_ml);
+    *err = hipGetLastError();
+  }
+  return nb;
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_context_len) {
-  const size_t pieces = static_cast<size_t>(batch) * num_q_heads * max_splits_for(max_context_len);
+  // Sized for the smallest piece (the most pieces); larger pieces need less.
+  const size_t pieces = static_cast<size_t>(batch) * num_q_heads *
+                        max_splits_for(max_context_len, __builtin_ctz(kDecodeSplit));
   return pieces * (kHeadDim + 2) * sizeof(float);
 }
 
@@ -489,20 +586,22 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t block_size,
                          int32_t max_context_len, float scale, void* workspace,
                          hipStream_t stream) {
-  const int max_splits = max_splits_for(max_context_len);
-  const size_t pieces = static_cast<size_t>(batch) * num_q_heads * max_splits;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_ml = ws_o + pieces * kHeadDim;
   const int log2_bs = __builtin_ctz(static_cast<unsigned>(block_size));
   const float scale_log2 = scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
   hipError_t err = hipSuccess;
+  // Consecutive launches over slices of the sequences, in stream order, each
+  // using the workspace from its start (the previous slice is merged by then).
+  for (int b0 = 0; b0 < batch && err == hipSuccess;) {
+    const int64_t row = static_cast<int64_t>(b0) * num_q_heads * kHeadDim;
+    int done = 0;
 #define PA_DECODE_CASE(GG, CC)                                                              \
   case GG:                                                                                 \
-    err = launch_split<GG, CC>(out, q, k_cache, v_cache, block_table, block_table_stride,  \
-                               context_lens, batch, num_q_heads, num_kv_heads, log2_bs,    \
-                               max_context_len, scale_log2, max_splits, ws_o, ws_ml,       \
-                               stream);                                                    \
+    done = launch_split<GG, CC>(out + row, q + row, k_cache, v_cache,                      \
+                                block_table + static_cast<int64_t>(b0) * block_table_stride, \
+                                block_table_stride, context_lens + b0, batch - b0,         \
+                                num_q_heads, num_kv_heads, log2_bs, max_context_len,       \
+                                scale_log2, static_cast<float*>(workspace), stream, &err); \
     break;
   switch (G) {
     PA_DECODE_CASE(1, 8)
@@ -513,13 +612,8 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
       return hipErrorInvalidValue;
   }
 #undef PA_DECODE_CASE
-  if (err != hipSuccess) return err;
-  if (max_splits > 1) {
-    hipLaunchKernelGGL(decode_reduce_kernel,
-                       dim3(static_cast<uint32_t>(static_cast<int64_t>(batch) * num_q_heads)),
-                       dim3(kHeadDim), 0, stream, out, context_lens, num_q_heads, max_context_len,
-                       max_splits, ws_o, ws_ml);
-    err = hipGetLastError();
+    if (done <= 0) return hipErrorInvalidValue;
+    b0 += done;
   }
   return err;
 }
