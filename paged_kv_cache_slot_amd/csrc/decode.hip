@@ -2,16 +2,20 @@
 // keys and values sit in fixed-size blocks reached through the sequence's
 // block table ("DeepSeek研究员1200行代码复刻vLLM…", section "vLLM是什么？").
 //
-// Work split. Each context is cut into pieces of kDecodeSplit (256) tokens; an
-// item is one (piece, kv head) with all G = Hq/Hkv query heads that read that
-// kv head, so every K/V byte is fetched from HBM once. A work-group is a single
-// wavefront and a persistent worker: the grid holds as many as fit on the GPU
-// at once, and they take items round-robin. Item w is piece p = w / Hkv of the
-// concatenated pieces of all sequences and kv head w % Hkv (the kv heads of a
-// piece are neighbours, so the same token rows are read together). The list
-// is never materialised: each wavefront scans context_lens into LDS prefix sums
-// and binary-searches the sequence of p, so nothing is spent on the empty
-// tail of a short sequence.
+// Work split. Each context is cut into pieces of 512 tokens (64 blocks if
+// that is less); an item is one (piece, kv head) with all G = Hq/Hkv query
+// heads that read that kv head, so every K/V byte is fetched from HBM once.
+// The grid is one work-group per CU (as many wavefronts as fit), resident
+// together. Every work-group derives the same global order of the items from
+// context_lens -- all full pieces, then each sequence's partial last piece --
+// with a cost per item (its 32-token chunks plus one), and takes the items
+// whose first cost unit falls in its 1/grid share: all work-groups get the
+// same cost to within one item, with no atomics in global memory. It keeps
+// them in an LDS table, largest first, and its wavefronts take them from an
+// LDS counter: wavefronts that run faster take more, and the small items come
+// last, so they all finish together. (A counter in global memory is no good:
+// under full HBM load its returned value arrives so late that the in-order
+// vmcnt accounting stalls every load issued after it.)
 //
 // Within an item, each row of 16 lanes takes every fourth token and each lane
 // a 16-byte slice (8 elements of head_dim) of that token's 256-byte kv-head
@@ -19,8 +23,8 @@
 // chunks of CH groups of 4 tokens held in two alternating register buffers:
 // the loads of the next chunk -- or of the next item's first chunk, whose
 // block ids and q were fetched one item ahead -- are in flight while the
-// current chunk is computed, so HBM requests never stop. There is no barrier:
-// wavefronts never wait for each other.
+// current chunk is computed, so HBM requests never stop. After building the
+// item table there is no barrier: wavefronts never wait for each other.
 //
 // Per token: q.k from four v_dot2c_f32_bf16 per lane, summed over the 16-lane
 // row with DPP; online softmax in base 2 (scale*log2e folded in), updated once
