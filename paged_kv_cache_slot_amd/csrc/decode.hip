@@ -74,10 +74,10 @@ struct Item {
   int valid, b, g, split, L, nsplit;
 };
 
-// Wavefronts per work-group: all that fit on a CU at once (two per SIMD, one
-// for G = 8, whose register use allows only one).
+// Wavefronts per work-group: all that fit on a CU at once: three per SIMD for
+// G <= 2 (chunks of 4 token groups), two for G = 4, one for G = 8.
 template <int G>
-constexpr int decode_waves() { return G >= 8 ? 4 : 8; }
+constexpr int decode_waves() { return G >= 8 ? 4 : (G <= 2 ? 12 : 8); }
 
 template <int G, int CH>
 __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
@@ -608,8 +608,8 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                                 scale_log2, static_cast<float*>(workspace), stream, &err); \
     break;
   switch (G) {
-    PA_DECODE_CASE(1, 8)
-    PA_DECODE_CASE(2, 8)
+    PA_DECODE_CASE(1, 4)
+    PA_DECODE_CASE(2, 4)
     PA_DECODE_CASE(4, 4)
     PA_DECODE_CASE(8, 2)
     default:
