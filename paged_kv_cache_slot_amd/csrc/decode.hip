@@ -2,8 +2,8 @@
 // keys and values sit in fixed-size blocks reached through the sequence's
 // block table ("DeepSeek研究员1200行代码复刻vLLM…", section "vLLM是什么？").
 //
-// Work split. Each context is cut into pieces of 512 tokens (64 blocks if
-// that is less); an item is one (piece, kv head) with all G = Hq/Hkv query
+// Work split. Each context is cut into pieces of 512 or 1024 tokens (64 blocks at most,
+// see launch_split); an item is one (piece, kv head) with all G = Hq/Hkv query
 // heads that read that kv head, so every K/V byte is fetched from HBM once.
 // The grid is one work-group per CU (as many wavefronts as fit), resident
 // together. Every work-group derives the same global order of the items from
@@ -47,6 +47,7 @@ namespace {
 constexpr int kScanRows = 1024;        // rows of context_lens held in LDS at a time
 constexpr int kMaxGroupItems = 4096;   // items one work-group can own (LDS table)
 constexpr int kSizeClasses = 16;       // item-size classes of the largest-first order
+constexpr float kLazyLog2 = 8.f;       // headroom of the softmax reference (log2 units)
 
 // Merges (m2, l2, acc2) into (m, l, acc): base-2 online-softmax states.
 template <int N>
@@ -351,13 +352,18 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
       float cm = s[0][hh];
 #pragma unroll
       for (int j = 1; j < CH; ++j) cm = fmaxf(cm, s[j][hh]);
-      const float mn = fmaxf(m[hh], cm);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(m[hh] - mu);
-      m[hh] = mn;
-      l[hh] *= alpha;
+      // m is the reference of this lane's (acc, l), -inf until it sees a token.
+      // It is raised only when a chunk's maximum exceeds it by more than
+      // kLazyLog2, so p <= 2^kLazyLog2 and the rescale is rare.
+      const bool raise = cm > m[hh] + kLazyLog2;
+      if (__any(raise)) {
+        const float alpha = raise ? fast_exp2(m[hh] - cm) : 1.f;  // 0 from -inf
+        m[hh] = raise ? cm : m[hh];
+        l[hh] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
+        for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
+      }
+      const float mu = m[hh] == -INFINITY ? 0.f : m[hh];  // no token yet: every s is -inf
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         const float p = fast_exp2(s[j][hh] - mu);
@@ -477,28 +483,34 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   }
 }
 
-// Merges the pieces of sequences with more than one piece: one work-group per
-// (sequence, query head), one thread per element of head_dim.
-__global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(
-    uint16_t* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t num_q_heads,
-    int32_t max_context_len, int32_t max_splits, int32_t log2_split,
+// Merges the pieces of sequences with more than one piece: one wavefront per
+// (sequence, query head), two elements of head_dim per lane, four wavefronts
+// per work-group.
+constexpr int kReduceRows = 4;
+__global__ __launch_bounds__(64 * kReduceRows) void decode_reduce_kernel(
+    uint16_t* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t rows,
+    int32_t num_q_heads, int32_t max_context_len, int32_t max_splits, int32_t log2_split,
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml) {
-  const int64_t bh = blockIdx.x;
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * kReduceRows + (threadIdx.x >> 6);
+  if (bh >= rows) return;
   const int b = static_cast<int>(bh / num_q_heads);
   const int L = min(context_lens[b], max_context_len);
   const int nsplit = min((L + (1 << log2_split) - 1) >> log2_split, max_splits);
   if (nsplit <= 1) return;  // written by the split kernel (or a padding row)
-  const int d = threadIdx.x;
+  const int d = (threadIdx.x & 63) * 2;
   const float* ml = ws_ml + bh * max_splits * 2;
   float M = -INFINITY;
   for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
-  float o = 0.f, lt = 0.f;
+  float o0 = 0.f, o1 = 0.f, lt = 0.f;
   for (int i = 0; i < nsplit; ++i) {
     const float a = fast_exp2(ml[2 * i] - M);
+    const float2 v = *reinterpret_cast<const float2*>(ws_o + (bh * max_splits + i) * kHeadDim + d);
     lt += a * ml[2 * i + 1];
-    o += a * ws_o[(bh * max_splits + i) * kHeadDim + d];
+    o0 += a * v.x;
+    o1 += a * v.y;
   }
-  out[bh * kHeadDim + d] = static_cast<uint16_t>(pack_bf16x2(o / lt, 0.f) & 0xffffu);
+  const float inv = 1.f / lt;
+  *reinterpret_cast<uint32_t*>(out + bh * kHeadDim + d) = pack_bf16x2(o0 * inv, o1 * inv);
 }
 
 // Pieces per context of max_context_len tokens, for pieces of 2^log2_split.
@@ -531,9 +543,8 @@ int resident_groups() {
 // One launch of the split kernel (and the reduce, if needed) over the first
 // sequences of `batch`: at most kScanRows of them, and few enough that no
 // work-group can own more than kMaxGroupItems items (a work-group's share of
-// the cost, over the cheapest item's cost). Pieces are 512 tokens, or 64
-// blocks if that is less. Returns the number of sequences handled (the caller
-// goes on with the rest).
+// the cost, over the cheapest item's cost). Returns the number of sequences
+// handled (the caller goes on with the rest).
 template <int G, int CH>
 int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                  const uint16_t* v_cache, const int32_t* block_table, int32_t bt_stride,
@@ -542,7 +553,12 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                  float* workspace, hipStream_t stream, hipError_t* err) {
   constexpr int W = decode_waves<G>();
   const int groups = resident_groups<G, CH>();
-  const int log2_split = std::min(9, log2_bs + 6);
+  // 512-token pieces; 1024 for batches of more than 4096 (sequence, kv head)
+  // pairs, whose work-groups own enough items that the per-item cost matters
+  // more than the finer balance (measured: configs 2 and 3 prefer 512, the
+  // 1024-sequence block-16 batch 1024). Never more than 64 blocks.
+  const int log2_split =
+      std::min(static_cast<int64_t>(batch) * num_kv_heads > 4096 ? 10 : 9, log2_bs + 6);
   const int64_t per_seq = static_cast<int64_t>(num_kv_heads) *
                           max_splits_for(max_context_len, log2_split) *
                           ((1 << (log2_split - 5)) + 1);  // items x highest item cost
@@ -566,10 +582,12 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                      max_splits, log2_split, ws_o, ws_ml, 0);
   *err = hipGetLastError();
   if (*err == hipSuccess && max_splits > 1) {
+    const int64_t rows = static_cast<int64_t>(nb) * num_q_heads;
     hipLaunchKernelGGL(decode_reduce_kernel,
-                       dim3(static_cast<uint32_t>(static_cast<int64_t>(nb) * num_q_heads)),
-                       dim3(kHeadDim), 0, stream, out, context_lens, num_q_heads,
-                       max_context_len, max_splits, log2_split, ws_o, ws_ml);
+                       dim3(static_cast<uint32_t>((rows + kReduceRows - 1) / kReduceRows)),
+                       dim3(64 * kReduceRows), 0, stream, out, context_lens,
+                       static_cast<int32_t>(rows), num_q_heads, max_context_len, max_splits,
+                       log2_split, ws_o, ws_ml);
     *err = hipGetLastError();
   }
   return nb;

@@ -112,7 +112,7 @@ DECODE_GRID = [
 @pytest.mark.parametrize("bs,hq,hkv,lens", DECODE_GRID,
                          ids=[f"bs{a}-hq{b}-hkv{c}" for a, b, c, _ in DECODE_GRID])
 def test_decode_grid_all_rows(bs, hq, hkv, lens):
-    """Several 256-token pieces, ragged tails, padding rows, every GQA ratio."""
+    """Several pieces, ragged tails, padding rows, every GQA ratio."""
     say(f"[case] decode grid bs={bs} Hq={hq} Hkv={hkv} lens={lens}")
     case = workloads.decode_case(len(lens), (1, 2048), hq, hkv, 128, bs, seed=77 + bs + hq,
                                  device=DEV, lens=lens, spare_blocks=5)
@@ -127,6 +127,26 @@ def test_decode_grid_all_rows(bs, hq, hkv, lens):
     for b, L in enumerate(lens):
         if L == 0:
             assert int(out[b].float().abs().sum()) == 0
+
+
+def test_decode_large_batch_long_pieces():
+    """520 rows x 8 kv heads (more than 4096 pairs, so pieces of 1024 tokens),
+    lengths on and around the piece boundaries, padding rows: every row."""
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, 2100, size=520)
+    lens[:12] = [1, 1023, 1024, 1025, 2047, 2048, 2049, 0, 511, 512, 513, 2099]
+    say("[case] decode 520 rows, bs=32, Hq=16, Hkv=8, lengths U[1,2100) + boundaries")
+    case = workloads.decode_case(520, (1, 2100), 16, 8, 128, 32, seed=41, device=DEV,
+                                 lens=lens)
+    h = host_copy(case)
+    gpu_store(case)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
+                        nthreads=ORACLE_THREADS)
+    compare(out, ref, "decode 520 rows")
+    assert int(out[7].float().abs().sum()) == 0
 
 
 def test_decode_more_rows_than_one_scan_window():
