@@ -110,12 +110,12 @@ def run_timed(step, warmup, steps):
     return ms, [a.elapsed_time(b) for a, b in evs]
 
 
-def decode_bench(cid, warmup, steps):
+def decode_bench(name, warmup, steps):
     import torch
     import numpy as np
     import paged_kv_cache_slot_amd as pa
     import workloads
-    case = workloads.config_case(cid, device="cuda")
+    case = workloads.workload_case(name, device="cuda")
     B, hq, d = case["q"].shape
     out = torch.empty_like(case["q"])
     ws = torch.empty(pa.pa_decode_workspace_bytes(B, hq, d, case["max_context_len"],
@@ -148,7 +148,7 @@ def prefill_bench(warmup, steps):
     import numpy as np
     import paged_kv_cache_slot_amd as pa
     import workloads
-    case = workloads.config_case(4, device="cuda")
+    case = workloads.workload_case("qwen3_8b_prefill_prefix", device="cuda")
     out = torch.empty_like(case["q"])
     torch.cuda.synchronize()
 
@@ -192,7 +192,7 @@ def cpu_baseline(case):
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"the whole step once: store of {case['batch']} new tokens + fp64 "
                       f"attention for all {case['batch']} rows x {case['num_q_heads']} heads "
-                      f"(config 2, {int(np.asarray(case['lens']).sum())} context tokens)"}
+                      f"(qwen3_0.6b_decode, {int(np.asarray(case['lens']).sum())} context tokens)"}
 
 
 def main():
@@ -227,8 +227,8 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)} "
         f"({torch.cuda.get_device_properties(0).gcnArchName})")
 
-    log("[bench] config 2: store + decode")
-    main_res = decode_bench(2, args.warmup, args.steps)
+    log("[bench] qwen3_0.6b_decode: store + decode")
+    main_res = decode_bench("qwen3_0.6b_decode", args.warmup, args.steps)
     case = main_res["case"]
     digest = source_digest("decode.hip", "pa_internal.h")
     traffic = measured_traffic("pa_decode", digest)
@@ -242,22 +242,21 @@ def main():
 
     secondary = []
     if not args.no_secondary:
-        for cid in (3, 5):
-            log(f"[bench] config {cid}: store + decode")
-            r = decode_bench(cid, args.warmup, args.steps)
+        for name in ("qwen3_8b_decode", "bs16_stress_decode"):
+            log(f"[bench] {name}: store + decode")
+            r = decode_bench(name, args.warmup, args.steps)
             secondary.append({
-                "workload": workloads.CONFIGS[cid]["name"],
-                "config": cid, "ms_per_step": round(r["ms_per_step"], 4),
+                "workload": name, "ms_per_step": round(r["ms_per_step"], 4),
                 "step_GBps": round(r["gbs"], 2),
                 "decode_us": round(r["decode_ms"] * 1e3, 2),
                 "decode_GBps": round(r["decode_gbs"], 2),
                 "decode_frac_hbm": round(r["decode_gbs"] / HBM_PEAK_GBS, 4)})
             del r
             torch.cuda.empty_cache()
-        log("[bench] config 4: store + prefill")
+        log("[bench] qwen3_8b_prefill_prefix: store + prefill")
         r = prefill_bench(args.warmup, args.steps)
         secondary.append({
-            "workload": "qwen3_8b_prefill_prefix", "config": 4,
+            "workload": "qwen3_8b_prefill_prefix",
             "ms_per_step": round(r["ms_per_step"], 4), "prefill_us": round(r["prefill_ms"] * 1e3, 2),
             "prefill_TFLOPs": round(r["tflops"], 2),
             "prefill_frac_mfma": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),

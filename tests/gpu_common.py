@@ -105,10 +105,10 @@ def sample_rows(lens, n, seed):
     return np.array(sorted(pick), dtype=np.int32)
 
 
-def make_config(cid, **over):
+def make_case(name, **over):
     """Full-size (or overridden) case generated on the GPU, plus host copies."""
-    say(f"[case] config {cid} ({workloads.CONFIGS[cid]['name']}) seed {workloads.seed_of(cid)} "
+    say(f"[case] workload {name} seed {workloads.seed_of(name)} "
         f"overrides {over}")
-    case = workloads.config_case(cid, device=DEV, **over)
+    case = workloads.workload_case(name, device=DEV, **over)
     torch.cuda.synchronize()
     return case, host_copy(case)

@@ -14,7 +14,7 @@ import oracle
 import paged_kv_cache_slot_amd as pa
 import workloads
 from tests.gpu_common import (DEV, compare, gpu_decode, gpu_prefill, gpu_store, host_copy,
-                              make_config, oracle_after_store, require_gpu, sample_rows, say,
+                              make_case, oracle_after_store, require_gpu, sample_rows, say,
                               ORACLE_THREADS)
 
 pytestmark = pytest.mark.gpu
@@ -31,10 +31,12 @@ def _pool_bits(t):
 
 # ------------------------------------------------------------------ store --
 
-@pytest.mark.parametrize("cid", [1, 3, 5, 4])
-def test_store_bit_exact_full_pool(cid):
-    """Whole-pool memcmp after the store, -1 rows included (configs 3 and 5 pad)."""
-    case, h = make_config(cid)
+@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_8b_decode", "bs16_stress_decode",
+                                  "qwen3_8b_prefill_prefix"])
+def test_store_bit_exact_full_pool(name):
+    """Whole-pool memcmp after the store, -1 rows included (the Qwen3-8B and
+    block-16 decode workloads pad)."""
+    case, h = make_case(name)
     say(f"  pa_store_kvcache T={case['slot_mapping'].numel()} "
         f"(-1 rows: {int((h['slot_mapping'] < 0).sum())})")
     gpu_store(case)
@@ -78,21 +80,23 @@ def test_store_empty_is_noop():
 
 # ----------------------------------------------------------------- decode --
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 5])
-def test_decode_step_full_size(cid):
-    """store + decode on the full workload; every row for config 1, sampled rows
+@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_0.6b_decode", "qwen3_8b_decode",
+                                  "bs16_stress_decode"])
+def test_decode_step_full_size(name):
+    """store + decode on the full workload; every row for the tiny workload, sampled rows
     (longest, shortest, padding, 40 random) for the others."""
-    case, h = make_config(cid)
+    case, h = make_case(name)
     say(f"  pa_store_kvcache + pa_decode B={case['batch']} Hq={case['num_q_heads']} "
         f"Hkv={case['num_kv_heads']} bs={case['block_size']} max_len={case['max_context_len']}")
     gpu_store(case)
     out = gpu_decode(case)
     torch.cuda.synchronize()
     kc, vc = oracle_after_store(h)
-    rows = None if cid == 1 else sample_rows(h["lens"], 40, seed=cid)
+    rows = None if name == "tiny_decode" else sample_rows(h["lens"], 40,
+                                                          seed=workloads.seed_of(name))
     ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
                         rows=rows, nthreads=ORACLE_THREADS)
-    compare(out, ref, f"config {cid} decode", rows=rows)
+    compare(out, ref, f"{name} decode", rows=rows)
     pad = np.flatnonzero(h["lens"] == 0)
     if len(pad):
         assert int(out[torch.from_numpy(pad).to(DEV)].float().abs().sum()) == 0
@@ -210,7 +214,7 @@ def test_decode_block_permutation_bitwise():
 
 
 def test_decode_deterministic():
-    case = workloads.config_case(1, device=DEV)
+    case = workloads.workload_case("tiny_decode", device=DEV)
     a = gpu_decode(case)
     b = gpu_decode(case)
     torch.cuda.synchronize()
@@ -222,7 +226,7 @@ def test_decode_deterministic():
 def test_prefill_full_size_sampled():
     """Config 4 (64 sequences, cached prefixes from 8 shared chains): store the
     new tokens, run prefill, check 160 sampled query rows (all heads)."""
-    case, h = make_config(4)
+    case, h = make_case("qwen3_8b_prefill_prefix")
     say(f"  pa_store_kvcache + pa_prefill_varlen T={case['total_q']} "
         f"max_seqlen_q={case['max_seqlen_q']}")
     gpu_store(case)
@@ -237,7 +241,7 @@ def test_prefill_full_size_sampled():
     toks = np.array(sorted(toks), dtype=np.int32)
     ref = oracle.prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["context_lens"], h["block_table"],
                          h["scale"], tokens=toks, nthreads=ORACLE_THREADS)
-    compare(out, ref, "config 4 prefill", rows=toks)
+    compare(out, ref, "qwen3_8b_prefill_prefix prefill", rows=toks)
 
 
 PREFILL_GRID = [

@@ -6,20 +6,20 @@ import workloads
 
 
 def test_same_seed_same_bytes():
-    a = workloads.config_case(1)
-    b = workloads.config_case(1)
+    a = workloads.workload_case("tiny_decode")
+    b = workloads.workload_case("tiny_decode")
     for key in ("k_cache", "v_cache", "q", "k_new", "v_new", "block_table", "slot_mapping"):
         assert workloads.digest(a[key]) == workloads.digest(b[key]), key
-    c = workloads.config_case(1, seed=99)
+    c = workloads.workload_case("tiny_decode", seed=99)
     assert workloads.digest(a["q"]) != workloads.digest(c["q"])
 
 
-@pytest.mark.parametrize("cid", [1, 3, 5])
-def test_decode_metadata(cid):
-    cfg = workloads.CONFIGS[cid]
+@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_8b_decode", "bs16_stress_decode"])
+def test_decode_metadata(name):
+    cfg = workloads.WORKLOADS[name]
     # Small stand-ins keep the pool tiny on the CPU; the metadata rules are the same.
-    over = {} if cid == 1 else dict(batch=40, pad=4)
-    case = workloads.config_case(cid, **over)
+    over = {} if name == "tiny_decode" else dict(batch=40, pad=4)
+    case = workloads.workload_case(name, **over)
     bs = case["block_size"]
     lens = case["context_lens"].numpy()
     table = case["block_table"].numpy()
@@ -43,7 +43,7 @@ def test_decode_metadata(cid):
 
 
 def test_prefill_prefix_sharing():
-    case = workloads.config_case(4, batch=24)
+    case = workloads.workload_case("qwen3_8b_prefill_prefix", batch=24)
     bs = case["block_size"]
     table = case["block_table"].numpy()
     k = case["prefix_blocks"]

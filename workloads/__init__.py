@@ -27,30 +27,31 @@ import math
 import numpy as np
 import torch
 
-# The five workloads. Shapes follow the pages' benchmarks: Qwen3-0.6B with 256
-# sequences and lengths of 100..1024 tokens, Qwen3-8B with random lengths, and
-# the two block sizes the pages contrast (256 in nano-vLLM, 16 in vLLM).
-CONFIGS = {
-    1: dict(name="tiny_decode", kind="decode", batch=4, len_range=(100, 300),
+# The five workloads, by name. Shapes follow the pages' benchmarks: Qwen3-0.6B
+# with 256 sequences and lengths of 100..1024 tokens, Qwen3-8B with random
+# lengths, and the two block sizes the pages contrast (256 in nano-vLLM, 16 in
+# vLLM). Each has a fixed seed.
+WORKLOADS = {
+    "tiny_decode": dict(seed=1001, kind="decode", batch=4, len_range=(100, 300),
             num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
             num_blocks=16, pad=0, pad_at="tail"),
-    2: dict(name="qwen3_0.6b_decode", kind="decode", batch=256, len_range=(100, 2048),
+    "qwen3_0.6b_decode": dict(seed=1002, kind="decode", batch=256, len_range=(100, 2048),
             num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
             num_blocks=None, pad=0, pad_at="tail"),
-    3: dict(name="qwen3_8b_decode", kind="decode", batch=512, len_range=(200, 2048),
+    "qwen3_8b_decode": dict(seed=1003, kind="decode", batch=512, len_range=(200, 2048),
             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=256,
             num_blocks=None, pad=41, pad_at="tail"),
-    4: dict(name="qwen3_8b_prefill_prefix", kind="prefill", batch=64, new_range=(100, 1024),
+    "qwen3_8b_prefill_prefix": dict(seed=1004, kind="prefill", batch=64, new_range=(100, 1024),
             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=256,
             chains=8, chain_blocks=3),
-    5: dict(name="bs16_stress_decode", kind="decode", batch=1024, len_range=(100, 2048),
+    "bs16_stress_decode": dict(seed=1005, kind="decode", batch=1024, len_range=(100, 2048),
             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
             num_blocks=None, pad=102, pad_at="random"),
 }
 
 
-def seed_of(config_id):
-    return 1000 + config_id
+def seed_of(name):
+    return WORKLOADS[name]["seed"]
 
 
 def softmax_scale(head_dim):
@@ -208,11 +209,11 @@ def prefill_case(batch, new_range, num_q_heads, num_kv_heads, head_dim, block_si
     )
 
 
-def config_case(config_id, device="cpu", seed=None, **overrides):
-    """The inputs of workload `config_id` (1..5), optionally with fields overridden."""
-    cfg = dict(CONFIGS[config_id])
+def workload_case(name, device="cpu", seed=None, **overrides):
+    """The inputs of the named workload, optionally with fields overridden."""
+    cfg = dict(WORKLOADS[name])
     cfg.update(overrides)
-    seed = seed_of(config_id) if seed is None else seed
+    seed = cfg["seed"] if seed is None else seed
     if cfg["kind"] == "decode":
         return decode_case(cfg["batch"], cfg["len_range"], cfg["num_q_heads"],
                            cfg["num_kv_heads"], cfg["head_dim"], cfg["block_size"],
