@@ -59,6 +59,8 @@ extern "C" {
 #define PA_ERR_UNSUPPORTED (-3) /* valid but unsupported shape or alignment     */
 #define PA_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required   */
 #define PA_ERR_HIP (-5)         /* the HIP runtime reported an error on launch  */
+#define PA_ERR_NO_BLOCKS (-6)   /* block manager: not enough free blocks        */
+#define PA_ERR_SEQ (-7)         /* block manager: sequence id unknown or in use */
 
 /* Static text for a status code (never NULL). */
 const char* pa_status_string(int status);

@@ -10,6 +10,10 @@ raises.
   pa_store_kvcache   write new tokens' K/V into the paged pools (slot -1 skipped)
   pa_decode          one query token per sequence over its paged context
   pa_prefill_varlen  causal varlen prefill over a cached prefix plus new tokens
+
+The host-side block manager that produces their metadata (block tables, slot
+mappings, lengths) with chained-hash prefix caching is bound in
+`paged_kv_cache_slot_amd.block_manager`.
 """
 import ctypes
 import os
@@ -22,7 +26,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ("pa_status_string", "pa_store_kvcache", "pa_decode_workspace_bytes",
-                    "pa_decode", "pa_prefill_varlen", "pa_validate_metadata")
+                    "pa_decode", "pa_prefill_varlen", "pa_validate_metadata",
+                    # block manager (include/pa_block_manager.h, block_manager.py)
+                    "pa_xxh64", "pa_block_hash", "pa_bm_create", "pa_bm_destroy",
+                    "pa_bm_num_free_blocks", "pa_bm_can_allocate", "pa_bm_allocate",
+                    "pa_bm_can_append", "pa_bm_append", "pa_bm_append_batch", "pa_bm_deallocate", "pa_bm_seq_info",
+                    "pa_bm_block_table", "pa_bm_block_info", "pa_bm_stats",
+                    "pa_bm_prefill_metadata", "pa_bm_decode_metadata")
 
 _lib = None
 

@@ -4,10 +4,13 @@ Every HIP source is compiled with packed-fp32 code generation switched off
 (`-Xclang -target-feature -Xclang -packed-fp32-ops`); hipcc's host pass warns
 that it does not know that feature, which is harmless.
 
-LLVM's atomic optimizer is switched off: the only atomics are one-lane
-work-queue fetches whose result is needed a whole item later, and the
-optimizer's wave-wide rewrite reads the result back at once, which waits for
-every load in flight.
+LLVM's atomic optimizer is switched off: the decode kernel's only atomics are
+one-lane fetches of a work-group's LDS work counter whose result is needed a
+whole item later, and the optimizer's wave-wide rewrite reads the result back
+at once, which waits for every load in flight.
+
+Host-only C++ sources (the block manager) are compiled by the host compiler
+and linked into the same library.
 """
 import os
 import subprocess
@@ -21,6 +24,9 @@ LIB = os.path.join(HERE, "libpa.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["pa_api.hip", "store_kvcache.hip", "decode.hip", "prefill.hip"]
+HOST_SOURCES = ["block_manager.cpp"]
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -42,11 +48,21 @@ def _compile(src):
     return obj
 
 
+def _compile_host(src):
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0 or r.stderr.strip():
+        raise RuntimeError(f"{CXX} failed on {src}:\n{r.stderr}")
+    return obj
+
+
 def build(verbose=False):
     """Compiles every source and links libpa.so; returns the library path."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    jobs = [(_compile, s) for s in SOURCES] + [(_compile_host, s) for s in HOST_SOURCES]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: j[0](j[1]), jobs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -57,6 +57,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported shape or alignment";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch error";
+    case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
+    case PA_ERR_SEQ: return "sequence id unknown or already live";
     default: return "unknown status";
   }
 }

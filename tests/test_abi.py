@@ -1,6 +1,7 @@
-"""The C-ABI library on the host: it loads, exports what include/pa.h declares,
+"""The C-ABI library on the host: it loads, exports what include/*.h declare,
 and rejects bad arguments before touching the GPU. No kernel runs here."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -12,15 +13,18 @@ import paged_kv_cache_slot_amd as pa
 import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, -1, -2, -3, -4
 
 
 def declared_functions():
-    with open(HEADER) as f:
-        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        with open(header) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -42,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, -5):
+    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, -5, -6, -7):
         assert pa.pa_status_string(code) not in ("", "unknown status")
     assert pa.pa_status_string(1234) == "unknown status"
 
@@ -111,16 +115,16 @@ def test_workspace_size():
     assert pa.pa_decode_workspace_bytes(0, 4, 128, 257, 16) == 0
 
 
-@pytest.mark.parametrize("cid", [1, 4])
-def test_validate_metadata_accepts_generated(cid):
-    case = workloads.config_case(cid, **({} if cid == 1 else dict(batch=12)))
+@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_8b_prefill_prefix"])
+def test_validate_metadata_accepts_generated(name):
+    case = workloads.workload_case(name, **({} if name == "tiny_decode" else dict(batch=12)))
     pa.pa_validate_metadata(case["block_table"], case["context_lens"], case["num_blocks"],
                             case["block_size"], cu_seqlens_q=case.get("cu_seqlens_q"),
                             slot_mapping=case["slot_mapping"])
 
 
 def test_validate_metadata_rejects():
-    case = workloads.config_case(3, batch=20, pad=2)
+    case = workloads.workload_case("qwen3_8b_decode", batch=20, pad=2)
     bt = case["block_table"].numpy().copy()
     cl = case["context_lens"].numpy().copy()
     sm = case["slot_mapping"].numpy().copy()
