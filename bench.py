@@ -17,7 +17,10 @@ The same JSON line carries:
   secondary     the other workloads of the pages: Qwen3-8B-shaped decode
                 (512 rows, 41 padding), block-16 stress decode (1024 rows),
                 and Qwen3-8B-shaped varlen prefill with cached prefixes
-                (TFLOP/s against the bf16 MFMA peak).
+                (TFLOP/s against the bf16 MFMA peak);
+  block_manager host cost of the C++ block manager per decode step (batched
+                append + decode metadata for 256 sequences) and per
+                allocation, beside the oracle's Python manager.
 Progress goes to stderr; stdout holds only the JSON line.
 """
 import argparse
@@ -170,6 +173,68 @@ def prefill_bench(warmup, steps):
                 tflops=flops / (kern_ms * 1e-3) / 1e12, total_q=case["total_q"])
 
 
+def block_manager_bench(decode_steps=256, oracle_steps=8):
+    """Host cost of the block manager on the Qwen3-0.6B decode shape: 256
+    sequences, block_size 256, prompts of U[100,1024] tokens of which 0..3
+    leading blocks come from one of 8 shared prefix chains.
+
+    native   the C++ calls timed by the `bm_bench` executable (no Python in
+             the loop): allocation, decode steps of one batched append plus
+             the step's decode metadata, prefill metadata, XXH64 throughput;
+    binding  the same decode step through the Python binding, reusing its
+             output arrays (what a Python scheduler pays per step);
+    oracle   the oracle's plain Python manager: allocation of the batch and
+             `oracle_steps` decode steps."""
+    import subprocess
+    import numpy as np
+    from paged_kv_cache_slot_amd.block_manager import BlockManager
+    from paged_kv_cache_slot_amd.build import BM_BENCH
+    if not os.path.exists(BM_BENCH):
+        raise RuntimeError(f"{BM_BENCH} is missing: run __graft_entry__.build()")
+    native = json.loads(subprocess.run([BM_BENCH, "256", "256", str(decode_steps)],
+                                       check=True, capture_output=True, text=True).stdout)
+    B, bs, vocab = 256, 256, 151936
+    rng = np.random.default_rng(4242)
+    chains = rng.integers(0, vocab, size=(8, 3 * bs))
+    prompts = []
+    for _ in range(B):
+        n = int(rng.integers(100, 1025))
+        k = min(int(rng.integers(0, 4)), n // bs)
+        head = chains[int(rng.integers(0, 8))][:k * bs]
+        prompts.append(np.concatenate([head, rng.integers(0, vocab, size=n - k * bs)])
+                       .astype(np.int32))
+    gen = rng.integers(0, vocab, size=(decode_steps, B)).astype(np.int32)
+    stride = -(-(max(len(p) for p in prompts) + decode_steps) // bs)
+    num_blocks = sum(-(-(len(p) + decode_steps) // bs) for p in prompts) + 64
+    ids = np.arange(B, dtype=np.int64)
+
+    bm = BlockManager(num_blocks, bs)
+    for i, p in enumerate(prompts):
+        bm.allocate(i, p)
+    out = (np.empty(B, np.int32), np.empty(B, np.int32), np.empty((B, stride), np.int32))
+    t0 = time.perf_counter()
+    for s in range(decode_steps):
+        bm.append_batch(ids, gen[s])
+        bm.decode_metadata(ids, B, stride, out=out)
+    t_step = (time.perf_counter() - t0) / decode_steps
+
+    import oracle.block_manager as obm
+    ob = obm.BlockManager(num_blocks, bs)
+    t0 = time.perf_counter()
+    for i, p in enumerate(prompts):
+        ob.allocate(i, p.tolist())
+    o_alloc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for s in range(oracle_steps):
+        ob.append_batch(list(range(B)), gen[s].tolist())
+        ob.decode_metadata(list(range(B)), B, stride)
+    o_step = (time.perf_counter() - t0) / oracle_steps
+    return {"native": native,
+            "binding": {"decode_step_us": round(t_step * 1e6, 2), "steps": decode_steps},
+            "oracle": {"allocate_us_per_seq": round(o_alloc / B * 1e6, 1),
+                       "decode_step_us": round(o_step * 1e6, 1), "steps": oracle_steps}}
+
+
 def cpu_baseline(case):
     """The oracle (plain fp64 C++) on the same decode step, on the host cores:
     the KV store of the new tokens, then attention for every row."""
@@ -263,6 +328,11 @@ def main():
             "algorithmic_flops": r["flops"], "total_q": r["total_q"]})
         torch.cuda.empty_cache()
 
+    log("[bench] block manager (host)")
+    bmr = block_manager_bench()
+    bmr["native_step_frac_of_gpu_step"] = round(bmr["native"]["decode_step_us"] * 1e-3
+                                                / main_res["ms_per_step"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
@@ -282,6 +352,7 @@ def main():
                    "head_dim": case["head_dim"], "seed": case["seed"],
                    "step_bytes": main_res["step_bytes"]},
         "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+        "block_manager": bmr,
     }
     print(json.dumps(line), flush=True)
 

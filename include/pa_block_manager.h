@@ -167,6 +167,16 @@ int pa_bm_block_info(const pa_block_manager* bm, int32_t block, int32_t* ref_cou
 int pa_bm_stats(const pa_block_manager* bm, int64_t* out);
 
 /*
+ * Sizes of a batch of live sequences, for sizing metadata buffers (any output
+ * pointer may be NULL): the total and largest count of tokens past the cached
+ * prefix (prefill query rows), the largest length and the largest block count.
+ * PA_ERR_SEQ for an id that is not live.
+ */
+int pa_bm_batch_info(const pa_block_manager* bm, const int64_t* seq_ids, int32_t batch,
+                     int64_t* new_tokens, int32_t* max_new_tokens, int32_t* max_len,
+                     int32_t* max_blocks);
+
+/*
  * Builds the metadata of a prefill batch over live sequences seq_ids[0..batch)
  * (normally just allocated): sequence b contributes its tokens past the cached
  * prefix, N_b = len - num_cached_tokens, as query rows.

@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = ("pa_status_string", "pa_store_kvcache", "pa_decode_workspace
                     "pa_bm_num_free_blocks", "pa_bm_can_allocate", "pa_bm_allocate",
                     "pa_bm_can_append", "pa_bm_append", "pa_bm_append_batch", "pa_bm_deallocate", "pa_bm_seq_info",
                     "pa_bm_block_table", "pa_bm_block_info", "pa_bm_stats",
-                    "pa_bm_prefill_metadata", "pa_bm_decode_metadata")
+                    "pa_bm_batch_info", "pa_bm_prefill_metadata", "pa_bm_decode_metadata")
 
 _lib = None
 

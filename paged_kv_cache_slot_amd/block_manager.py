@@ -38,6 +38,7 @@ def _lib():
             "pa_bm_block_table": ([p, i64, p, i32], ctypes.c_int),
             "pa_bm_block_info": ([p, i32, p, p, p], ctypes.c_int),
             "pa_bm_stats": ([p, p], ctypes.c_int),
+            "pa_bm_batch_info": ([p, p, i32, p, p, p, p], ctypes.c_int),
             "pa_bm_prefill_metadata": ([p, p, i32, p, p, p, i32, p, i32, p, p], ctypes.c_int),
             "pa_bm_decode_metadata": ([p, p, i32, i32, p, p, p, i32, p], ctypes.c_int),
         }
@@ -54,7 +55,24 @@ def _ptr(a):
 
 
 def _i32(a):
+    """C-contiguous int32 array (no copy when `a` already is one)."""
+    if isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous:
+        return a
     return np.ascontiguousarray(np.asarray(a, dtype=np.int64).astype(np.int32))
+
+
+def _ids(a):
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+def _out(arr, shape, name):
+    """A caller-provided int32 output array of exactly `shape`, or a new one."""
+    if arr is None:
+        return np.empty(shape, np.int32)
+    if (not isinstance(arr, np.ndarray) or arr.dtype != np.int32 or arr.shape != tuple(shape)
+            or not arr.flags.c_contiguous):
+        raise ValueError(f"{name} must be a C-contiguous int32 array of shape {tuple(shape)}")
+    return arr
 
 
 def _check(name, rc):
@@ -126,7 +144,7 @@ class BlockManager:
 
     def append_batch(self, seq_ids, tokens):
         """One token per sequence, all or nothing (pa_bm_append_batch)."""
-        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        ids = _ids(seq_ids)
         t = _i32(tokens)
         if len(ids) != len(t):
             raise ValueError("one token per sequence id")
@@ -162,14 +180,23 @@ class BlockManager:
         _check("pa_bm_stats", self._lib.pa_bm_stats(self._h, _ptr(out)))
         return dict(zip(self.STAT_NAMES, (int(x) for x in out)))
 
+    def batch_info(self, seq_ids):
+        """(new_tokens, max_new_tokens, max_len, max_blocks) of live sequences."""
+        ids = _ids(seq_ids)
+        nt, mq, ml, mb = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_bm_batch_info", self._lib.pa_bm_batch_info(
+            self._h, _ptr(ids), len(ids), ctypes.byref(nt), ctypes.byref(mq), ctypes.byref(ml),
+            ctypes.byref(mb)))
+        return nt.value, mq.value, ml.value, mb.value
+
     def prefill_metadata(self, seq_ids, block_table_stride, slot_capacity=None):
         """(cu_seqlens_q, context_lens, slot_mapping, block_table, total_q,
         max_seqlen_q) as numpy int32 arrays and ints. slot_capacity defaults to
         the exact total."""
-        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        ids = _ids(seq_ids)
         B = len(ids)
         if slot_capacity is None:
-            slot_capacity = sum(self.seq_info(s)[0] - self.seq_info(s)[1] for s in ids)
+            slot_capacity = self.batch_info(ids)[0]
         cu = np.zeros(B + 1, np.int32)
         ctx = np.zeros(max(B, 1), np.int32)
         slots = np.zeros(max(int(slot_capacity), 1), np.int32)
@@ -181,16 +208,18 @@ class BlockManager:
         return (cu, ctx[:B], slots[:int(slot_capacity)], bt[:B, :int(block_table_stride)],
                 tq.value, mq.value)
 
-    def decode_metadata(self, seq_ids, padded_batch, block_table_stride):
-        """(context_lens, slot_mapping, block_table, max_context_len)."""
-        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
-        B = len(ids)
-        P = int(padded_batch)
-        ctx = np.zeros(max(P, 1), np.int32)
-        slots = np.zeros(max(P, 1), np.int32)
-        bt = np.zeros((max(P, 1), max(int(block_table_stride), 1)), np.int32)
+    def decode_metadata(self, seq_ids, padded_batch, block_table_stride, out=None):
+        """(context_lens, slot_mapping, block_table, max_context_len).
+
+        `out` may hold three int32 arrays ([P], [P], [P, stride]) to fill in
+        place, so a decode loop allocates nothing per step."""
+        ids = _ids(seq_ids)
+        B, P, S = len(ids), int(padded_batch), int(block_table_stride)
+        o = out or (None, None, None)
+        ctx = _out(o[0], (P,), "context_lens")
+        slots = _out(o[1], (P,), "slot_mapping")
+        bt = _out(o[2], (P, S), "block_table")
         mx = ctypes.c_int32()
         _check("pa_bm_decode_metadata", self._lib.pa_bm_decode_metadata(
-            self._h, _ptr(ids), B, P, _ptr(ctx), _ptr(slots), _ptr(bt), int(block_table_stride),
-            ctypes.byref(mx)))
-        return ctx[:P], slots[:P], bt[:P, :int(block_table_stride)], mx.value
+            self._h, _ptr(ids), B, P, _ptr(ctx), _ptr(slots), _ptr(bt), S, ctypes.byref(mx)))
+        return ctx, slots, bt, mx.value

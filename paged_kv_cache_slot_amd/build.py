@@ -10,7 +10,8 @@ whole item later, and the optimizer's wave-wide rewrite reads the result back
 at once, which waits for every load in flight.
 
 Host-only C++ sources (the block manager) are compiled by the host compiler
-and linked into the same library.
+and linked into the same library; `bm_bench`, the block manager's host
+benchmark executable, is linked from the same object.
 """
 import os
 import subprocess
@@ -21,6 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
+BM_BENCH = os.path.join(HERE, "bm_bench")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["pa_api.hip", "store_kvcache.hip", "decode.hip", "prefill.hip"]
@@ -69,6 +71,16 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # The block manager's host benchmark (run by bench.py), linked statically
+    # against the same object file.
+    host_objs = [o for o in objs if os.path.basename(o) in
+                 {os.path.splitext(h)[0] + ".o" for h in HOST_SOURCES}]
+    cmd = [CXX, *HOST_FLAGS, os.path.join(CSRC, "bm_bench.cpp"), *host_objs, "-o",
+           BM_BENCH + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0 or r.stderr.strip():
+        raise RuntimeError(f"{CXX} failed on bm_bench.cpp:\n{r.stderr}")
+    os.replace(BM_BENCH + ".tmp", BM_BENCH)
     if verbose:
         print(LIB)
     return LIB

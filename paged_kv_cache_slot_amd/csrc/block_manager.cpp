@@ -36,15 +36,19 @@ constexpr uint64_t kPrime5 = 0x27D4EB2F165667C5ull;
 
 inline uint64_t rotl64(uint64_t x, int r) { return (x << r) | (x >> (64 - r)); }
 
+// The hash is defined over little-endian words, which is the host's order.
+static_assert(__BYTE_ORDER__ == __ORDER_LITTLE_ENDIAN__, "little-endian host assumed");
+
 inline uint64_t read_le64(const uint8_t* p) {
-  uint64_t v = 0;
-  for (int i = 7; i >= 0; --i) v = (v << 8) | p[i];
+  uint64_t v;
+  std::memcpy(&v, p, sizeof(v));
   return v;
 }
 
 inline uint32_t read_le32(const uint8_t* p) {
-  return static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8) |
-         (static_cast<uint32_t>(p[2]) << 16) | (static_cast<uint32_t>(p[3]) << 24);
+  uint32_t v;
+  std::memcpy(&v, p, sizeof(v));
+  return v;
 }
 
 inline uint64_t lane_round(uint64_t acc, uint64_t input) {
@@ -104,17 +108,15 @@ uint64_t xxh64(const uint8_t* p, size_t len, uint64_t seed) {
   return h;
 }
 
-// Serialises (parent, tokens) as le64 || le32... into `buf` and hashes it.
+// Serialises (parent, tokens) as le64 || le32... into `buf` and hashes it
+// (on the little-endian host both are their in-memory bytes).
 uint64_t chained_hash(std::vector<uint8_t>& buf, bool has_parent, uint64_t parent,
                       const int32_t* tokens, int32_t n) {
-  buf.clear();
-  buf.reserve(8 + 4 * static_cast<size_t>(n));
-  if (has_parent)
-    for (int i = 0; i < 8; ++i) buf.push_back(static_cast<uint8_t>(parent >> (8 * i)));
-  for (int32_t t = 0; t < n; ++t) {
-    const uint32_t u = static_cast<uint32_t>(tokens[t]);
-    for (int i = 0; i < 4; ++i) buf.push_back(static_cast<uint8_t>(u >> (8 * i)));
-  }
+  const size_t head = has_parent ? sizeof(parent) : 0;
+  const size_t body = sizeof(int32_t) * static_cast<size_t>(n);
+  buf.resize(head + body);
+  if (has_parent) std::memcpy(buf.data(), &parent, head);
+  if (body) std::memcpy(buf.data() + head, tokens, body);
   return xxh64(buf.data(), buf.size(), 0);
 }
 
@@ -134,6 +136,7 @@ struct Seq {
   std::vector<int32_t> table;    // physical block of each logical block
   std::vector<uint64_t> hashes;  // chained hash of each full logical block
   int32_t cached = 0;            // leading tokens found in the cache at allocation
+  uint64_t stamp = 0;            // last batched call that named it (repeat check)
 };
 
 // What allocate would do with one logical block.
@@ -151,7 +154,10 @@ struct pa_block_manager {
   std::unordered_map<uint64_t, int32_t> index;
   std::unordered_map<int64_t, Seq> seqs;
   int64_t stats[5] = {0, 0, 0, 0, 0};
-  mutable std::vector<uint8_t> scratch;  // hash serialisation buffer
+  uint64_t epoch = 0;                         // counts batched appends
+  mutable std::vector<uint8_t> scratch;       // hash serialisation buffer
+  std::vector<Seq*> rows;                     // a batch's sequences, reused
+  mutable std::vector<const Seq*> crows;      // the same for read-only calls
 
   pa_block_manager(int32_t nb, int32_t bs)
       : num_blocks(nb), block_size(bs), blocks(nb), next(nb), prev(nb), in_free(nb, 0) {
@@ -398,18 +404,17 @@ int pa_bm_append_batch(pa_block_manager* bm, const int64_t* seq_ids, const int32
   if (batch < 0) return PA_ERR_SHAPE;
   if (batch == 0) return PA_OK;
   if (!seq_ids || !tokens) return PA_ERR_NULL;
-  std::vector<Seq*> rows(batch);
+  std::vector<Seq*>& rows = bm->rows;
+  rows.resize(batch);
+  const uint64_t epoch = ++bm->epoch;
   int64_t need = 0;
   for (int32_t b = 0; b < batch; ++b) {
     auto it = bm->seqs.find(seq_ids[b]);
-    if (it == bm->seqs.end()) return PA_ERR_SEQ;
+    if (it == bm->seqs.end() || it->second.stamp == epoch) return PA_ERR_SEQ;
     rows[b] = &it->second;
+    rows[b]->stamp = epoch;
     if (rows[b]->tokens.size() % bm->block_size == 0) ++need;
   }
-  std::vector<Seq*> sorted_rows(rows);
-  std::sort(sorted_rows.begin(), sorted_rows.end());
-  if (std::adjacent_find(sorted_rows.begin(), sorted_rows.end()) != sorted_rows.end())
-    return PA_ERR_SEQ;
   if (need > bm->num_free) return PA_ERR_NO_BLOCKS;
   for (int32_t b = 0; b < batch; ++b) append_token(bm, *rows[b], tokens[b]);
   return PA_OK;
@@ -471,6 +476,31 @@ int pa_bm_stats(const pa_block_manager* bm, int64_t* out) {
   return PA_OK;
 }
 
+int pa_bm_batch_info(const pa_block_manager* bm, const int64_t* seq_ids, int32_t batch,
+                     int64_t* new_tokens, int32_t* max_new_tokens, int32_t* max_len,
+                     int32_t* max_blocks) {
+  if (!bm) return PA_ERR_NULL;
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch > 0 && !seq_ids) return PA_ERR_NULL;
+  int64_t total = 0;
+  int32_t mq = 0, ml = 0, mb = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    auto it = bm->seqs.find(seq_ids[b]);
+    if (it == bm->seqs.end()) return PA_ERR_SEQ;
+    const Seq& s = it->second;
+    const int32_t len = static_cast<int32_t>(s.tokens.size());
+    total += len - s.cached;
+    mq = std::max(mq, len - s.cached);
+    ml = std::max(ml, len);
+    mb = std::max(mb, static_cast<int32_t>(s.table.size()));
+  }
+  if (new_tokens) *new_tokens = total;
+  if (max_new_tokens) *max_new_tokens = mq;
+  if (max_len) *max_len = ml;
+  if (max_blocks) *max_blocks = mb;
+  return PA_OK;
+}
+
 int pa_bm_prefill_metadata(const pa_block_manager* bm, const int64_t* seq_ids, int32_t batch,
                            int32_t* cu_seqlens_q, int32_t* context_lens,
                            int32_t* slot_mapping, int32_t slot_capacity, int32_t* block_table,
@@ -481,7 +511,8 @@ int pa_bm_prefill_metadata(const pa_block_manager* bm, const int64_t* seq_ids, i
   if (batch > 0 && !seq_ids) return PA_ERR_NULL;
   if (slot_capacity > 0 && !slot_mapping) return PA_ERR_NULL;
   // Check every sequence before writing anything.
-  std::vector<const Seq*> rows(batch);
+  std::vector<const Seq*>& rows = bm->crows;
+  rows.resize(batch);
   int64_t total = 0;
   int32_t max_q = 0;
   for (int32_t b = 0; b < batch; ++b) {
@@ -499,7 +530,12 @@ int pa_bm_prefill_metadata(const pa_block_manager* bm, const int64_t* seq_ids, i
   for (int32_t b = 0; b < batch; ++b) {
     const Seq& s = *rows[b];
     const int32_t len = static_cast<int32_t>(s.tokens.size());
-    for (int32_t pos = s.cached; pos < len; ++pos) slot_mapping[t++] = slot_of(bm, s, pos);
+    const int32_t bs = bm->block_size;
+    for (int32_t pos = s.cached; pos < len;) {  // one block at a time
+      const int32_t base = s.table[pos / bs] * bs;
+      const int32_t end = std::min(len, (pos / bs + 1) * bs);
+      for (int32_t off = pos % bs; pos < end; ++pos, ++off) slot_mapping[t++] = base + off;
+    }
     cu_seqlens_q[b + 1] = t;
     context_lens[b] = len;
     int32_t* row = block_table + static_cast<int64_t>(b) * block_table_stride;
@@ -520,7 +556,8 @@ int pa_bm_decode_metadata(const pa_block_manager* bm, const int64_t* seq_ids, in
   if (!bm || !context_lens || !slot_mapping || !block_table) return PA_ERR_NULL;
   if (batch < 0 || padded_batch < batch || block_table_stride < 0) return PA_ERR_SHAPE;
   if (batch > 0 && !seq_ids) return PA_ERR_NULL;
-  std::vector<const Seq*> rows(batch);
+  std::vector<const Seq*>& rows = bm->crows;
+  rows.resize(batch);
   for (int32_t b = 0; b < batch; ++b) {
     auto it = bm->seqs.find(seq_ids[b]);
     if (it == bm->seqs.end()) return PA_ERR_SEQ;

@@ -333,6 +333,15 @@ def test_native_matches_oracle_op_for_op(seed, num_blocks, bs):
         c, s, t, _ = nb.decode_metadata(live, len(live) + 3, stride)
         assert (c.tolist(), s.tolist(), t.tolist()) == ob.decode_metadata(live, len(live) + 3,
                                                                           stride)
+        rows = [len(ob.seqs[x]["tokens"]) - ob.seqs[x]["cached"] for x in live]
+        assert nb.batch_info(live) == (sum(rows), max(rows),
+                                       max(len(ob.seqs[x]["tokens"]) for x in live),
+                                       stride - 1)
+        P = len(live) + 1
+        out = (np.full(P, 7, np.int32), np.full(P, 7, np.int32), np.full((P, stride), 7, np.int32))
+        c, s, t, _ = nb.decode_metadata(live, P, stride, out=out)
+        assert c is out[0] and s is out[1] and t is out[2]
+        assert (c.tolist(), s.tolist(), t.tolist()) == ob.decode_metadata(live, P, stride)
         cu, c, s, t, _, _ = nb.prefill_metadata(live, stride)
         assert (cu.tolist(), c.tolist(), s.tolist(), t.tolist()) == ob.prefill_metadata(live,
                                                                                         stride)
