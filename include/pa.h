@@ -182,6 +182,75 @@ int pa_validate_metadata(const int32_t* block_table, int32_t block_table_stride,
                          int32_t max_context_len, char* detail,
                          size_t detail_len);
 
+/*
+ * Decode-step graphs: one HIP graph per batch-size bucket, each holding a
+ * whole decode step (pa_store_kvcache of the step's new tokens, then
+ * pa_decode) captured once and replayed with a single launch.
+ * [Report] "nano-vllm 深度分析报告", section "创新之处" (graph capture at a
+ * few batch sizes only, a batch rounded up to the next captured size, captured
+ * from the largest size down with one memory pool shared by all graphs) and
+ * table "可复用的模式与技巧", rows on the discrete batch sizes and on
+ * slot_mapping -1 padding.
+ *
+ * Every graph reads and writes the same caller-owned device buffers, sized for
+ * the largest bucket; that single set of buffers is what the shared pool is in
+ * the pages, and the graphs allocate no device memory of their own. Before a
+ * replay for `batch` rows the caller writes rows [0, bucket) of the inputs,
+ * with rows past `batch` as padding: context length 0 and slot -1 (what
+ * pa_bm_decode_metadata writes for padded_batch = bucket); their q, k_new and
+ * v_new rows may hold anything finite and their output rows come back zero.
+ * Rows [0, bucket) of `out` are written. Every context length of a replay
+ * must be <= max_context_len given at creation.
+ */
+typedef struct pa_decode_step_buffers {
+  void* out;                   /* [B][num_q_heads][head_dim] bf16                */
+  const void* q;               /* [B][num_q_heads][head_dim] bf16                */
+  const void* k_new;           /* [B][kv_token_stride] bf16 (first Hkv*D used)   */
+  const void* v_new;           /* [B][kv_token_stride] bf16                      */
+  int64_t kv_token_stride;     /* multiple of 8, >= num_kv_heads*head_dim       */
+  void* k_cache;               /* [num_blocks][block_size][Hkv][head_dim] bf16   */
+  void* v_cache;
+  const int32_t* slot_mapping; /* [B]                                            */
+  const int32_t* context_lens; /* [B]                                            */
+  const int32_t* block_table;  /* [B][block_table_stride]                        */
+  int32_t block_table_stride;
+  void* workspace;             /* >= pa_decode_workspace_bytes(B, Hq, D, max_context_len, bs) */
+  size_t workspace_bytes;
+  int32_t num_blocks, block_size, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_context_len;     /* bound of every replay's context lengths       */
+  float scale;                 /* softmax scale, positive and finite            */
+} pa_decode_step_buffers;
+/* B = the largest bucket. */
+
+typedef struct pa_decode_graphs pa_decode_graphs;
+
+/*
+ * Captures one graph per bucket, largest first. buckets[0..num_buckets) must
+ * be strictly increasing and >= 1; buckets == NULL means 1, 2, 4, ..., 512.
+ * The buffers are checked as pa_store_kvcache and pa_decode check theirs, for
+ * the largest bucket. Nothing runs on the GPU during creation (capture only
+ * records). Creation allocates host-side graph objects, not device memory; it
+ * must not itself be called inside a stream capture. *graphs receives the
+ * handle (NULL on failure).
+ */
+int pa_decode_graphs_create(const pa_decode_step_buffers* buffers, const int32_t* buckets,
+                            int32_t num_buckets, pa_decode_graphs** graphs);
+
+/* The smallest bucket >= batch (1 <= batch <= the largest), else PA_ERR_SHAPE. */
+int pa_decode_graphs_bucket(const pa_decode_graphs* graphs, int32_t batch, int32_t* bucket);
+
+/*
+ * Enqueues the decode step of `batch` rows on `stream` (NULL = the default
+ * stream) as one launch of the graph of its bucket; batch == 0 enqueues
+ * nothing, batch above the largest bucket is PA_ERR_SHAPE. Replays of graphs
+ * of one handle share the buffers: replays in flight at once on different
+ * streams race.
+ */
+int pa_decode_graphs_launch(pa_decode_graphs* graphs, int32_t batch, void* stream);
+
+/* Frees the graphs (NULL is ignored). Call it when no replay is in flight. */
+void pa_decode_graphs_destroy(pa_decode_graphs* graphs);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,8 @@ raises.
   pa_store_kvcache   write new tokens' K/V into the paged pools (slot -1 skipped)
   pa_decode          one query token per sequence over its paged context
   pa_prefill_varlen  causal varlen prefill over a cached prefix plus new tokens
+  pa_decode_graphs_create  HIP graphs of the whole decode step (store + decode)
+                     at a few batch-size buckets, replayed with one launch
 
 The host-side block manager that produces their metadata (block tables, slot
 mappings, lengths) with chained-hash prefix caching is bound in
@@ -20,7 +22,8 @@ import os
 
 __all__ = ["PAError", "library", "lib_path", "pa_store_kvcache", "pa_decode",
            "pa_decode_workspace_bytes", "pa_prefill_varlen", "pa_validate_metadata",
-           "pa_status_string", "EXPORTED_SYMBOLS"]
+           "pa_status_string", "pa_decode_graphs_create", "DecodeGraphs", "DEFAULT_BUCKETS",
+           "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libpa.so")
@@ -32,9 +35,26 @@ EXPORTED_SYMBOLS = ("pa_status_string", "pa_store_kvcache", "pa_decode_workspace
                     "pa_bm_num_free_blocks", "pa_bm_can_allocate", "pa_bm_allocate",
                     "pa_bm_can_append", "pa_bm_append", "pa_bm_append_batch", "pa_bm_deallocate", "pa_bm_seq_info",
                     "pa_bm_block_table", "pa_bm_block_info", "pa_bm_stats",
-                    "pa_bm_batch_info", "pa_bm_prefill_metadata", "pa_bm_decode_metadata")
+                    "pa_bm_batch_info", "pa_bm_prefill_metadata", "pa_bm_decode_metadata",
+                    # decode-step graphs
+                    "pa_decode_graphs_create", "pa_decode_graphs_bucket",
+                    "pa_decode_graphs_launch", "pa_decode_graphs_destroy")
 
 _lib = None
+
+
+class _StepBuffers(ctypes.Structure):
+    """pa_decode_step_buffers (include/pa.h), field for field."""
+    _fields_ = [("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p),
+                ("v_new", ctypes.c_void_p), ("kv_token_stride", ctypes.c_int64),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("slot_mapping", ctypes.c_void_p), ("context_lens", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
 
 
 class PAError(RuntimeError):
@@ -70,6 +90,15 @@ def library():
         lib.pa_validate_metadata.argtypes = [p, i32, p, i32, p, p, i32, i32, i32, i32,
                                              ctypes.c_char_p, sz]
         lib.pa_validate_metadata.restype = ctypes.c_int
+        lib.pa_decode_graphs_create.argtypes = [ctypes.POINTER(_StepBuffers), p, i32,
+                                                ctypes.POINTER(ctypes.c_void_p)]
+        lib.pa_decode_graphs_create.restype = ctypes.c_int
+        lib.pa_decode_graphs_bucket.argtypes = [p, i32, ctypes.POINTER(i32)]
+        lib.pa_decode_graphs_bucket.restype = ctypes.c_int
+        lib.pa_decode_graphs_launch.argtypes = [p, i32, p]
+        lib.pa_decode_graphs_launch.restype = ctypes.c_int
+        lib.pa_decode_graphs_destroy.argtypes = [p]
+        lib.pa_decode_graphs_destroy.restype = None
         _lib = lib
     return _lib
 
@@ -204,3 +233,85 @@ def pa_validate_metadata(block_table, context_lens, num_blocks, block_size, cu_s
         int(block_size), int(max_context_len), msg, 256)
     if rc != 0:
         raise PAError("pa_validate_metadata", rc, msg.value.decode())
+
+
+DEFAULT_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
+
+
+class DecodeGraphs:
+    """Handle of pa_decode_graphs_create: keeps the step buffers alive while
+    the graphs that read them exist. bucket() and launch() call
+    pa_decode_graphs_bucket and pa_decode_graphs_launch; close() calls
+    pa_decode_graphs_destroy."""
+
+    def __init__(self, handle, buckets, tensors):
+        self._h = handle
+        self.buckets = tuple(buckets)
+        self._tensors = tensors
+
+    def bucket(self, batch):
+        b = ctypes.c_int32()
+        _check("pa_decode_graphs_bucket",
+               library().pa_decode_graphs_bucket(self._h, int(batch), ctypes.byref(b)))
+        return b.value
+
+    def launch(self, batch, stream=None):
+        _check("pa_decode_graphs_launch",
+               library().pa_decode_graphs_launch(self._h, int(batch), _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            library().pa_decode_graphs_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+def pa_decode_graphs_create(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, context_lens,
+                            block_table, workspace, max_context_len, scale, buckets=None):
+    """Captures the decode step at each bucket (default 1, 2, 4, ..., 512).
+
+    Static device buffers sized for the largest bucket B: out, q [B, Hq, D];
+    k_new, v_new [B, Hkv, D] (or [B, >= Hkv*D] rows with unit stride inside a
+    row); pools [NB, bs, Hkv, D]; slot_mapping, context_lens [B] int32;
+    block_table [B, stride] int32; workspace uint8 of at least
+    pa_decode_workspace_bytes(B, Hq, D, max_context_len, bs) bytes. Before
+    launch(batch) the caller fills rows [0, bucket(batch)) of the inputs,
+    padding rows with context length 0 and slot -1."""
+    import torch
+    bk = list(DEFAULT_BUCKETS if buckets is None else buckets)
+    B = bk[-1] if bk else 0
+    num_blocks, bs, hkv, d = _pool_shape(k_cache, v_cache)
+    hq = int(q.shape[1])
+    k2 = k_new.flatten(1) if k_new.dim() == 3 else k_new
+    v2 = v_new.flatten(1) if v_new.dim() == 3 else v_new
+    if k2.stride(1) != 1 or v2.stride(1) != 1 or k2.stride(0) != v2.stride(0):
+        raise ValueError("k_new and v_new rows must have unit element stride and equal strides")
+    for name, t, rows in (("out", out, B), ("q", q, B), ("k_new", k2, B), ("v_new", v2, B),
+                          ("slot_mapping", slot_mapping, B), ("context_lens", context_lens, B),
+                          ("block_table", block_table, B)):
+        if t.shape[0] < rows:
+            raise ValueError(f"{name} has {t.shape[0]} rows, the largest bucket needs {rows}")
+    if not (out.is_contiguous() and q.is_contiguous() and block_table.is_contiguous()):
+        raise ValueError("out, q and block_table must be contiguous")
+    sb = _StepBuffers(
+        out=_dev(out, "out", torch.bfloat16).value, q=_dev(q, "q", torch.bfloat16).value,
+        k_new=_dev(k2, "k_new", torch.bfloat16).value, v_new=_dev(v2, "v_new", torch.bfloat16).value,
+        kv_token_stride=int(k2.stride(0)),
+        k_cache=_dev(k_cache, "k_cache", torch.bfloat16).value,
+        v_cache=_dev(v_cache, "v_cache", torch.bfloat16).value,
+        slot_mapping=_dev(slot_mapping, "slot_mapping", torch.int32).value,
+        context_lens=_dev(context_lens, "context_lens", torch.int32).value,
+        block_table=_dev(block_table, "block_table", torch.int32).value,
+        block_table_stride=int(block_table.shape[1]),
+        workspace=_dev(workspace, "workspace").value,
+        workspace_bytes=int(workspace.numel() * workspace.element_size()),
+        num_blocks=num_blocks, block_size=bs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        max_context_len=int(max_context_len), scale=float(scale))
+    arr = (ctypes.c_int32 * len(bk))(*bk) if bk else None
+    handle = ctypes.c_void_p()
+    rc = library().pa_decode_graphs_create(ctypes.byref(sb), arr, len(bk), ctypes.byref(handle))
+    _check("pa_decode_graphs_create", rc)
+    return DecodeGraphs(handle.value, bk, (out, q, k2, v2, k_cache, v_cache, slot_mapping,
+                                           context_lens, block_table, workspace))

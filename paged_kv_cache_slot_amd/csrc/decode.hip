@@ -595,6 +595,16 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
 
 }  // namespace
 
+void prepare_decode(int32_t num_q_heads, int32_t num_kv_heads) {
+  switch (num_q_heads / num_kv_heads) {
+    case 1: resident_groups<1, 4>(); break;
+    case 2: resident_groups<2, 4>(); break;
+    case 4: resident_groups<4, 4>(); break;
+    case 8: resident_groups<8, 2>(); break;
+    default: break;
+  }
+}
+
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_context_len) {
   // Sized for the smallest piece (the most pieces); larger pieces need less.
   const size_t pieces = static_cast<size_t>(batch) * num_q_heads *

@@ -1,9 +1,11 @@
 // C ABI of libpa.so: host-side argument checks, then kernel launches on the
-// caller's stream. Nothing here allocates, frees or synchronises. The
+// caller's stream. Nothing here allocates device memory or synchronises; only
+// the decode-step graphs create host-side graph objects (at creation). The
 // operations and their sources are documented in include/pa.h.
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <vector>
 
 #include "pa.h"
@@ -207,5 +209,139 @@ int pa_validate_metadata(const int32_t* block_table, int32_t block_table_stride,
   write_detail(detail, detail_len, "ok");
   return PA_OK;
 }
+
+// ------------------------------------------------------ decode-step graphs --
+
+}  // extern "C"
+
+struct pa_decode_graphs {
+  pa_decode_step_buffers buf;
+  std::vector<int32_t> buckets;          // increasing
+  std::vector<hipGraph_t> graphs;        // one per bucket
+  std::vector<hipGraphExec_t> execs;
+
+  ~pa_decode_graphs() {
+    for (hipGraphExec_t e : execs)
+      if (e) (void)hipGraphExecDestroy(e);
+    for (hipGraph_t g : graphs)
+      if (g) (void)hipGraphDestroy(g);
+  }
+};
+
+namespace {
+
+// The checks pa_store_kvcache and pa_decode make, for `batch` rows of `b`.
+int check_step_buffers(const pa_decode_step_buffers& b, int32_t batch) {
+  if (b.block_table_stride <= 0 || b.max_context_len < 0 || b.num_blocks <= 0 ||
+      !valid_scale(b.scale))
+    return PA_ERR_SHAPE;
+  int st = check_heads(b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size);
+  if (st != PA_OK) return st;
+  if (static_cast<int64_t>(b.block_table_stride) * b.block_size < b.max_context_len)
+    return PA_ERR_SHAPE;
+  if (b.kv_token_stride < static_cast<int64_t>(b.num_kv_heads) * b.head_dim)
+    return PA_ERR_SHAPE;
+  if (!b.out || !b.q || !b.k_new || !b.v_new || !b.k_cache || !b.v_cache || !b.slot_mapping ||
+      !b.context_lens || !b.block_table)
+    return PA_ERR_NULL;
+  if (b.kv_token_stride % 8 != 0 || !aligned16(b.out) || !aligned16(b.q) ||
+      !aligned16(b.k_new) || !aligned16(b.v_new) || !aligned16(b.k_cache) ||
+      !aligned16(b.v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const size_t need = pa::decode_workspace_bytes(batch, b.num_q_heads, b.max_context_len);
+  if (!b.workspace || b.workspace_bytes < need || !aligned16(b.workspace))
+    return PA_ERR_WORKSPACE;
+  return PA_OK;
+}
+
+// Records the decode step for `batch` rows on `stream` (which is capturing).
+hipError_t record_step(const pa_decode_step_buffers& b, int32_t batch, hipStream_t stream) {
+  hipError_t e = pa::launch_store_kvcache(
+      static_cast<const uint16_t*>(b.k_new), static_cast<const uint16_t*>(b.v_new),
+      b.kv_token_stride, static_cast<uint16_t*>(b.k_cache), static_cast<uint16_t*>(b.v_cache),
+      b.slot_mapping, batch, b.num_kv_heads, stream);
+  if (e != hipSuccess) return e;
+  return pa::launch_decode(
+      static_cast<uint16_t*>(b.out), static_cast<const uint16_t*>(b.q),
+      static_cast<const uint16_t*>(b.k_cache), static_cast<const uint16_t*>(b.v_cache),
+      b.block_table, b.block_table_stride, b.context_lens, batch, b.num_q_heads,
+      b.num_kv_heads, b.block_size, b.max_context_len, b.scale, b.workspace, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_graphs_create(const pa_decode_step_buffers* buffers, const int32_t* buckets,
+                            int32_t num_buckets, pa_decode_graphs** graphs) {
+  if (!graphs) return PA_ERR_NULL;
+  *graphs = nullptr;
+  if (!buffers) return PA_ERR_NULL;
+  std::vector<int32_t> bk;
+  if (!buckets) {
+    for (int32_t x = 1; x <= 512; x *= 2) bk.push_back(x);
+  } else {
+    if (num_buckets < 1) return PA_ERR_SHAPE;
+    bk.assign(buckets, buckets + num_buckets);
+    for (size_t i = 0; i < bk.size(); ++i)
+      if (bk[i] < 1 || (i > 0 && bk[i] <= bk[i - 1])) return PA_ERR_SHAPE;
+  }
+  const int st = check_step_buffers(*buffers, bk.back());
+  if (st != PA_OK) return st;
+
+  auto* g = new (std::nothrow) pa_decode_graphs();
+  if (!g) return PA_ERR_HIP;
+  g->buf = *buffers;
+  g->buckets = bk;
+  g->graphs.assign(bk.size(), nullptr);
+  g->execs.assign(bk.size(), nullptr);
+  pa::prepare_decode(buffers->num_q_heads, buffers->num_kv_heads);
+  hipStream_t stream = nullptr;
+  if (hipStreamCreateWithFlags(&stream, hipStreamNonBlocking) != hipSuccess) {
+    delete g;
+    return PA_ERR_HIP;
+  }
+  int rc = PA_OK;
+  // Largest bucket first.
+  for (size_t i = bk.size(); i-- > 0 && rc == PA_OK;) {
+    if (hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+      rc = PA_ERR_HIP;
+      break;
+    }
+    const hipError_t rec = record_step(g->buf, bk[i], stream);
+    const hipError_t end = hipStreamEndCapture(stream, &g->graphs[i]);
+    if (rec != hipSuccess || end != hipSuccess ||
+        hipGraphInstantiate(&g->execs[i], g->graphs[i], nullptr, nullptr, 0) != hipSuccess)
+      rc = PA_ERR_HIP;
+  }
+  (void)hipStreamDestroy(stream);
+  if (rc != PA_OK) {
+    delete g;
+    return rc;
+  }
+  *graphs = g;
+  return PA_OK;
+}
+
+int pa_decode_graphs_bucket(const pa_decode_graphs* graphs, int32_t batch, int32_t* bucket) {
+  if (!graphs || !bucket) return PA_ERR_NULL;
+  for (int32_t b : graphs->buckets)
+    if (b >= batch && batch >= 1) {
+      *bucket = b;
+      return PA_OK;
+    }
+  return PA_ERR_SHAPE;
+}
+
+int pa_decode_graphs_launch(pa_decode_graphs* graphs, int32_t batch, void* stream) {
+  if (!graphs) return PA_ERR_NULL;
+  if (batch == 0) return PA_OK;
+  for (size_t i = 0; i < graphs->buckets.size(); ++i)
+    if (graphs->buckets[i] >= batch && batch >= 1)
+      return from_hip(hipGraphLaunch(graphs->execs[i], static_cast<hipStream_t>(stream)));
+  return PA_ERR_SHAPE;
+}
+
+void pa_decode_graphs_destroy(pa_decode_graphs* graphs) { delete graphs; }
 
 }  // extern "C"

@@ -35,6 +35,11 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
 
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_context_len);
 
+// Runs the host-side queries launch_decode makes on first use for this head
+// grouping (occupancy of its kernel on the current device), so that a later
+// launch_decode inside a stream capture only records kernel launches.
+void prepare_decode(int32_t num_q_heads, int32_t num_kv_heads);
+
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                           const uint16_t* v_cache, const int32_t* cu_seqlens_q,
                           const int32_t* context_lens, const int32_t* block_table,

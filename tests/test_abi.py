@@ -146,3 +146,65 @@ def test_validate_metadata_rejects():
     cu = np.array([0, 5, 3] + [3] * 18, dtype=np.int32)
     with pytest.raises(pa.PAError, match="new tokens"):
         pa.pa_validate_metadata(bt, cl, nb, bs, cu_seqlens_q=cu)
+
+
+# ------------------------------------------------------ decode-step graphs --
+
+def test_step_buffers_layout_matches_c(tmp_path):
+    """The binding's ctypes structure has the C struct's size and field offsets."""
+    fields = [f for f, _ in pa._StepBuffers._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "pa.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(pa_decode_step_buffers));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(pa_decode_step_buffers, {f}));\n'
+                           for f in fields) + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", f"-I{ROOT}/include", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(pa._StepBuffers)
+    assert got[1:] == [getattr(pa._StepBuffers, f).offset for f in fields]
+
+
+def _step_buffers(**kw):
+    P = 0x10000
+    base = dict(out=P, q=P, k_new=P, v_new=P, kv_token_stride=1024, k_cache=P, v_cache=P,
+                slot_mapping=P, context_lens=P, block_table=P, block_table_stride=8,
+                workspace=P, workspace_bytes=pa.pa_decode_workspace_bytes(512, 16, 128, 2048, 256),
+                num_blocks=100, block_size=256, num_q_heads=16, num_kv_heads=8, head_dim=128,
+                max_context_len=2048, scale=0.088)
+    base.update(kw)
+    return pa._StepBuffers(**base)
+
+
+def test_decode_graphs_argument_checks(lib):
+    """Every failing check returns before any HIP call (nothing here reaches the GPU)."""
+    f = lib.pa_decode_graphs_create
+    h = ctypes.c_void_p(123)
+
+    def create(buckets=None, **kw):
+        arr = (ctypes.c_int32 * len(buckets))(*buckets) if buckets else None
+        return f(ctypes.byref(_step_buffers(**kw)), arr, len(buckets or []), ctypes.byref(h))
+
+    assert f(None, None, 0, ctypes.byref(h)) == PA_ERR_NULL and h.value is None
+    assert f(ctypes.byref(_step_buffers()), None, 0, None) == PA_ERR_NULL
+    assert create(buckets=[1, 2, 2]) == PA_ERR_SHAPE          # not increasing
+    assert create(buckets=[0, 4]) == PA_ERR_SHAPE
+    assert f(ctypes.byref(_step_buffers()), (ctypes.c_int32 * 1)(4), 0,
+             ctypes.byref(h)) == PA_ERR_SHAPE                   # empty bucket list
+    assert create(scale=0.0) == PA_ERR_SHAPE
+    assert create(num_q_heads=24) == PA_ERR_UNSUPPORTED        # G = 3
+    assert create(block_size=8) == PA_ERR_UNSUPPORTED
+    assert create(block_table_stride=7) == PA_ERR_SHAPE        # 7 * 256 < 2048
+    assert create(kv_token_stride=1000) == PA_ERR_SHAPE
+    assert create(kv_token_stride=1028) == PA_ERR_UNSUPPORTED
+    assert create(q=None) == PA_ERR_NULL
+    assert create(out=0x10002) == PA_ERR_UNSUPPORTED
+    # the default buckets end at 512 rows, so 512 rows of workspace are needed
+    assert create(workspace_bytes=pa.pa_decode_workspace_bytes(256, 16, 128, 2048, 256)) == \
+        PA_ERR_WORKSPACE
+    assert create(buckets=[1, 256], workspace=None) == PA_ERR_WORKSPACE
+    b = ctypes.c_int32()
+    assert lib.pa_decode_graphs_bucket(None, 4, ctypes.byref(b)) == PA_ERR_NULL
+    assert lib.pa_decode_graphs_launch(None, 4, None) == PA_ERR_NULL
+    lib.pa_decode_graphs_destroy(None)
