@@ -20,7 +20,10 @@ The same JSON line carries:
                 (TFLOP/s against the bf16 MFMA peak);
   block_manager host cost of the C++ block manager per decode step (batched
                 append + decode metadata for 256 sequences) and per
-                allocation, beside the oracle's Python manager.
+                allocation, beside the oracle's Python manager;
+  decode_graphs wall time per decode step replayed from HIP graphs against
+                the eager launches, at batches 1 .. 256, for dependent
+                (wait after every step) and pipelined steps.
 Progress goes to stderr; stdout holds only the JSON line.
 """
 import argparse
@@ -235,6 +238,91 @@ def block_manager_bench(decode_steps=256, oracle_steps=8):
                        "decode_step_us": round(o_step * 1e6, 1), "steps": oracle_steps}}
 
 
+def graph_bench(batches=(1, 4, 16, 64, 256), steps=200, warmup=10):
+    """Decode step replayed from HIP graphs against the same step launched
+    eagerly, per batch size, on the Qwen3-0.6B decode shape (16 q / 8 kv
+    heads, block_size 256, context lengths U[100,2048], permuted blocks).
+    Both paths are driven from Python the way a serving loop would: eager =
+    pa_store_kvcache + pa_decode per step, graph = one pa_decode_graphs_launch
+    per step. Two patterns, wall-clock microseconds per step over `steps`
+    steps: dependent (the host waits for every step, as a decode loop that
+    samples from each step must) and pipelined (steps enqueued back to back,
+    one wait at the end)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_slot_amd as pa
+    B, hq, hkv, d, bs, max_len = 512, 16, 8, 128, 256, 2048
+    stride = max_len // bs
+    nb = B * stride + 8
+    g = torch.Generator(device="cuda").manual_seed(5150)
+    rnd = lambda *shape: torch.randn(*shape, generator=g, device="cuda").to(torch.bfloat16)
+    kc, vc = rnd(nb, bs, hkv, d), rnd(nb, bs, hkv, d)
+    q, kn, vn = rnd(B, hq, d), rnd(B, hkv, d), rnd(B, hkv, d)
+    out = torch.empty(B, hq, d, dtype=torch.bfloat16, device="cuda")
+    slots = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    table = torch.full((B, stride), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(pa.pa_decode_workspace_bytes(B, hq, d, max_len, bs), dtype=torch.uint8,
+                     device="cuda")
+    scale = 1.0 / np.sqrt(d)
+    graphs = pa.pa_decode_graphs_create(out, q, kn, vn, kc, vc, slots, lens, table, ws, max_len,
+                                        scale)
+    rng = np.random.default_rng(5150)
+    res = []
+    for batch in batches:
+        bucket = graphs.bucket(batch)
+        L = np.zeros(bucket, np.int32)
+        L[:batch] = rng.integers(100, max_len + 1, size=batch)
+        perm = rng.permutation(nb)
+        t = np.full((bucket, stride), -1, np.int32)
+        sm = np.full(bucket, -1, np.int32)
+        used = 0
+        for b in range(batch):
+            n = -(-int(L[b]) // bs)
+            t[b, :n] = perm[used:used + n]
+            used += n
+            sm[b] = t[b, (L[b] - 1) // bs] * bs + (L[b] - 1) % bs
+        lens[:bucket].copy_(torch.from_numpy(L))
+        slots[:bucket].copy_(torch.from_numpy(sm))
+        table[:bucket].copy_(torch.from_numpy(t))
+
+        def eager():
+            pa.pa_store_kvcache(kn[:batch], vn[:batch], kc, vc, slots[:batch])
+            pa.pa_decode(out[:batch], q[:batch], kc, vc, table[:batch], lens[:batch], max_len,
+                         scale, ws)
+
+        def graph():
+            graphs.launch(batch)
+
+        row = {"batch": batch, "bucket": bucket}
+        for name, fn in (("eager", eager), ("graph", graph)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            # Dependent steps: the host waits for each step before the next, as
+            # a serving loop must (the next step's tokens come from this one).
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+                torch.cuda.synchronize()
+            row[f"{name}_dependent_us"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+            # Pipelined steps: enqueued back to back, one wait at the end.
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            row[f"{name}_pipelined_us"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+        row["dependent_speedup"] = round(row["eager_dependent_us"] / row["graph_dependent_us"], 3)
+        row["pipelined_speedup"] = round(row["eager_pipelined_us"] / row["graph_pipelined_us"], 3)
+        res.append(row)
+    graphs.close()
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"shape": "16 q / 8 kv heads, head_dim 128, block_size 256, context U[100,2048], "
+                     "buckets 1..512 (powers of two), captured max_context_len 2048",
+            "steps": steps, "per_batch": res}
+
+
 def cpu_baseline(case):
     """The oracle (plain fp64 C++) on the same decode step, on the host cores:
     the KV store of the new tokens, then attention for every row."""
@@ -328,6 +416,11 @@ def main():
             "algorithmic_flops": r["flops"], "total_q": r["total_q"]})
         torch.cuda.empty_cache()
 
+    graphs = None
+    if not args.no_secondary:
+        log("[bench] decode-step graphs vs eager")
+        graphs = graph_bench()
+
     log("[bench] block manager (host)")
     bmr = block_manager_bench()
     bmr["native_step_frac_of_gpu_step"] = round(bmr["native"]["decode_step_us"] * 1e-3
@@ -352,7 +445,7 @@ def main():
                    "head_dim": case["head_dim"], "seed": case["seed"],
                    "step_bytes": main_res["step_bytes"]},
         "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
-        "block_manager": bmr,
+        "block_manager": bmr, "decode_graphs": graphs,
     }
     print(json.dumps(line), flush=True)
 
