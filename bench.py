@@ -21,6 +21,8 @@ The same JSON line carries:
   block_manager host cost of the C++ block manager per decode step (batched
                 append + decode metadata for 256 sequences) and per
                 allocation, beside the oracle's Python manager;
+  sampler       Gumbel-max sampling of 256 tokens from a 151936-entry
+                vocabulary (GB/s of probabilities against HBM peak);
   decode_graphs wall time per decode step replayed from HIP graphs against
                 the eager launches, at batches 1 .. 256, for dependent
                 (wait after every step) and pipelined steps.
@@ -323,6 +325,46 @@ def graph_bench(batches=(1, 4, 16, 64, 256), steps=200, warmup=10):
             "steps": steps, "per_batch": res}
 
 
+def sampler_bench(warmup, steps, B=256, V=151936):
+    """Gumbel-max sampling of one token per row from fp32 probabilities:
+    256 rows of a Qwen3-sized vocabulary (151936), softmax of N(0,1) logits.
+    Algorithmic bytes: every probability read once and one int32 token written
+    per row. The oracle (numpy Philox + fp32 keys) is timed on 8 rows."""
+    import numpy as np
+    import torch
+    import oracle.sampler as osm
+    import paged_kv_cache_slot_amd as pa
+    g = torch.Generator(device="cuda").manual_seed(404)
+    probs = torch.softmax(torch.randn(B, V, generator=g, device="cuda"), dim=1).contiguous()
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(pa.pa_sample_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        pa.pa_sample_gumbel(tok, probs, 1, i, ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        pa.pa_sample_gumbel(tok, probs, 1, warmup + i, ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = B * V * 4 + B * 4
+    sample_rows = 8
+    pc = probs[:sample_rows].cpu().numpy()
+    t0 = time.perf_counter()
+    osm.sample(pc, 1, 0, rows=np.arange(sample_rows))
+    dt = time.perf_counter() - t0
+    return {"workload": f"gumbel-max sampling, {B} rows x vocab {V}, fp32 probabilities",
+            "us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes,
+            "Gelem_per_s": round(B * V / (us * 1e-6) / 1e9, 2),
+            "oracle": {"Gelem_per_s": round(sample_rows * V / dt / 1e9, 5), "rows": sample_rows,
+                       "cores": 1}}
+
+
 def cpu_baseline(case):
     """The oracle (plain fp64 C++) on the same decode step, on the host cores:
     the KV store of the new tokens, then attention for every row."""
@@ -416,8 +458,10 @@ def main():
             "algorithmic_flops": r["flops"], "total_q": r["total_q"]})
         torch.cuda.empty_cache()
 
-    graphs = None
+    graphs = sampler = None
     if not args.no_secondary:
+        log("[bench] gumbel-max sampler")
+        sampler = sampler_bench(args.warmup, args.steps)
         log("[bench] decode-step graphs vs eager")
         graphs = graph_bench()
 
@@ -445,7 +489,7 @@ def main():
                    "head_dim": case["head_dim"], "seed": case["seed"],
                    "step_bytes": main_res["step_bytes"]},
         "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
-        "block_manager": bmr, "decode_graphs": graphs,
+        "block_manager": bmr, "decode_graphs": graphs, "sampler": sampler,
     }
     print(json.dumps(line), flush=True)
 

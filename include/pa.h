@@ -183,6 +183,42 @@ int pa_validate_metadata(const int32_t* block_table, int32_t block_table_stride,
                          size_t detail_len);
 
 /*
+ * pa_sample_gumbel -- draw one token per row from per-row probabilities by
+ * Gumbel-max sampling: the index of the largest p / E with E ~ Exp(1).
+ * [Report] "nano-vllm 深度分析报告", section "创新之处" (the Gumbel-Max item:
+ * divide the probabilities by Exp(1) draws and take the argmax instead of a
+ * multinomial draw) and table "可复用的模式与技巧", row "Gumbel-Max 采样".
+ *
+ *   For row b and element i < vocab, with x the 32-bit word i mod 4 of
+ *   Philox4x32-10 (Salmon et al., SC'11) at counter
+ *   (i / 4, b, offset mod 2^32, offset / 2^32) and key (seed mod 2^32, seed / 2^32):
+ *     u   = ((x >> 9) + 1/2) * 2^-23            (exact fp32, in (0, 1))
+ *     E   = -log2(u)                            (a positive multiple of an Exp(1)
+ *                                                variable: same argmax)
+ *     key = p[b,i] / E                          (fp32; the kernel uses hardware
+ *                                                log2 and reciprocal, within ~2
+ *                                                ulp of exactly rounded steps)
+ *     tokens[b] = the index of the largest key, the smallest index among equal
+ *                 keys (a row of zeros gives 0).
+ *   The same (seed, offset) gives the same draws; use a new offset per step.
+ *
+ *   probs      [batch][row_stride] fp32 device array, 4-byte aligned,
+ *              row_stride >= vocab (rows that start 16-byte aligned, i.e. a
+ *              16-byte aligned base and row_stride a multiple of 4, are read
+ *              with 16-byte loads); entries must be non-negative and finite
+ *              (they need not sum to 1: the draw is proportional to p).
+ *   tokens     [batch] int32 device array.
+ *   workspace  device scratch of pa_sample_workspace_bytes(batch, vocab)
+ *              bytes, 8-byte aligned; no initialisation needed.
+ *   batch in [0, 65535]; vocab >= 1. batch == 0 enqueues nothing.
+ */
+size_t pa_sample_workspace_bytes(int32_t batch, int32_t vocab);
+
+int pa_sample_gumbel(int32_t* tokens, const float* probs, int64_t row_stride, int32_t batch,
+                     int32_t vocab, uint64_t seed, uint64_t offset, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * Decode-step graphs: one HIP graph per batch-size bucket, each holding a
  * whole decode step (pa_store_kvcache of the step's new tokens, then
  * pa_decode) captured once and replayed with a single launch.

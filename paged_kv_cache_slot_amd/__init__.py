@@ -10,6 +10,7 @@ raises.
   pa_store_kvcache   write new tokens' K/V into the paged pools (slot -1 skipped)
   pa_decode          one query token per sequence over its paged context
   pa_prefill_varlen  causal varlen prefill over a cached prefix plus new tokens
+  pa_sample_gumbel   Gumbel-max token sampling from per-row probabilities
   pa_decode_graphs_create  HIP graphs of the whole decode step (store + decode)
                      at a few batch-size buckets, replayed with one launch
 
@@ -22,7 +23,8 @@ import os
 
 __all__ = ["PAError", "library", "lib_path", "pa_store_kvcache", "pa_decode",
            "pa_decode_workspace_bytes", "pa_prefill_varlen", "pa_validate_metadata",
-           "pa_status_string", "pa_decode_graphs_create", "DecodeGraphs", "DEFAULT_BUCKETS",
+           "pa_status_string", "pa_sample_workspace_bytes", "pa_sample_gumbel",
+           "pa_decode_graphs_create", "DecodeGraphs", "DEFAULT_BUCKETS",
            "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +38,8 @@ EXPORTED_SYMBOLS = ("pa_status_string", "pa_store_kvcache", "pa_decode_workspace
                     "pa_bm_can_append", "pa_bm_append", "pa_bm_append_batch", "pa_bm_deallocate", "pa_bm_seq_info",
                     "pa_bm_block_table", "pa_bm_block_info", "pa_bm_stats",
                     "pa_bm_batch_info", "pa_bm_prefill_metadata", "pa_bm_decode_metadata",
+                    # sampler
+                    "pa_sample_workspace_bytes", "pa_sample_gumbel",
                     # decode-step graphs
                     "pa_decode_graphs_create", "pa_decode_graphs_bucket",
                     "pa_decode_graphs_launch", "pa_decode_graphs_destroy")
@@ -90,6 +94,11 @@ def library():
         lib.pa_validate_metadata.argtypes = [p, i32, p, i32, p, p, i32, i32, i32, i32,
                                              ctypes.c_char_p, sz]
         lib.pa_validate_metadata.restype = ctypes.c_int
+        lib.pa_sample_workspace_bytes.argtypes = [i32, i32]
+        lib.pa_sample_workspace_bytes.restype = sz
+        lib.pa_sample_gumbel.argtypes = [p, p, i64, i32, i32, ctypes.c_uint64, ctypes.c_uint64,
+                                         p, sz, p]
+        lib.pa_sample_gumbel.restype = ctypes.c_int
         lib.pa_decode_graphs_create.argtypes = [ctypes.POINTER(_StepBuffers), p, i32,
                                                 ctypes.POINTER(ctypes.c_void_p)]
         lib.pa_decode_graphs_create.restype = ctypes.c_int
@@ -233,6 +242,32 @@ def pa_validate_metadata(block_table, context_lens, num_blocks, block_size, cu_s
         int(block_size), int(max_context_len), msg, 256)
     if rc != 0:
         raise PAError("pa_validate_metadata", rc, msg.value.decode())
+
+
+def pa_sample_workspace_bytes(batch, vocab):
+    return int(library().pa_sample_workspace_bytes(int(batch), int(vocab)))
+
+
+def pa_sample_gumbel(tokens, probs, seed, offset, workspace=None, stream=None):
+    """tokens: [B] int32; probs: [B, V] fp32 with unit stride inside a row.
+    Draws tokens[b] = argmax_i probs[b, i] / E[b, i], E ~ Exp(1) from Philox
+    at (seed, offset). workspace: uint8 tensor of pa_sample_workspace_bytes
+    bytes (allocated here if None)."""
+    import torch
+    if probs.dim() != 2 or probs.stride(1) != 1:
+        raise ValueError("probs must be [B, V] with unit stride inside a row")
+    B, V = int(probs.shape[0]), int(probs.shape[1])
+    if tokens.numel() != B:
+        raise ValueError("one token per row")
+    if workspace is None:
+        workspace = torch.empty(max(pa_sample_workspace_bytes(B, V), 8), dtype=torch.uint8,
+                                device=probs.device)
+    rc = library().pa_sample_gumbel(
+        _dev(tokens, "tokens", torch.int32), _dev(probs, "probs", torch.float32),
+        int(probs.stride(0)), B, V, int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+        _dev(workspace, "workspace"), int(workspace.numel() * workspace.element_size()),
+        _stream(stream))
+    _check("pa_sample_gumbel", rc)
 
 
 DEFAULT_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)

@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "libpa.so")
 BM_BENCH = os.path.join(HERE, "bm_bench")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["pa_api.hip", "store_kvcache.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pa_api.hip", "store_kvcache.hip", "decode.hip", "prefill.hip", "sampler.hip"]
 HOST_SOURCES = ["block_manager.cpp"]
 CXX = os.environ.get("CXX", "g++")
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]

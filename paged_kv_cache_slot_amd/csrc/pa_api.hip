@@ -210,6 +210,25 @@ int pa_validate_metadata(const int32_t* block_table, int32_t block_table_stride,
   return PA_OK;
 }
 
+size_t pa_sample_workspace_bytes(int32_t batch, int32_t vocab) {
+  return pa::sample_workspace_bytes(batch, vocab);
+}
+
+int pa_sample_gumbel(int32_t* tokens, const float* probs, int64_t row_stride, int32_t batch,
+                     int32_t vocab, uint64_t seed, uint64_t offset, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (batch < 0 || vocab < 1 || row_stride < vocab) return PA_ERR_SHAPE;
+  if (batch > 65535) return PA_ERR_UNSUPPORTED;
+  if (batch == 0) return PA_OK;
+  if (!tokens || !probs) return PA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(probs) & 3u) return PA_ERR_UNSUPPORTED;
+  const size_t need = pa::sample_workspace_bytes(batch, vocab);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+    return PA_ERR_WORKSPACE;
+  return from_hip(pa::launch_sample(tokens, probs, row_stride, batch, vocab, seed, offset,
+                                    workspace, static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------ decode-step graphs --
 
 }  // extern "C"

@@ -35,6 +35,12 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
 
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_context_len);
 
+size_t sample_workspace_bytes(int32_t batch, int32_t vocab);
+
+hipError_t launch_sample(int32_t* tokens, const float* probs, int64_t row_stride, int32_t batch,
+                         int32_t vocab, uint64_t seed, uint64_t offset, void* workspace,
+                         hipStream_t stream);
+
 // Runs the host-side queries launch_decode makes on first use for this head
 // grouping (occupancy of its kernel on the current device), so that a later
 // launch_decode inside a stream capture only records kernel launches.

@@ -208,3 +208,20 @@ def test_decode_graphs_argument_checks(lib):
     assert lib.pa_decode_graphs_bucket(None, 4, ctypes.byref(b)) == PA_ERR_NULL
     assert lib.pa_decode_graphs_launch(None, 4, None) == PA_ERR_NULL
     lib.pa_decode_graphs_destroy(None)
+
+
+def test_sample_argument_checks(lib):
+    f = lib.pa_sample_gumbel
+    P = _fake()
+    ws = pa.pa_sample_workspace_bytes(4, 1000)
+    assert ws == 4 * 1 * 8                                 # one tile per row, one chunk
+    assert pa.pa_sample_workspace_bytes(256, 151936) == 256 * 8 * 8
+    assert pa.pa_sample_workspace_bytes(1, 151936) == 149 * 8
+    assert f(P, P, 1000, 0, 1000, 1, 2, None, 0, None) == PA_OK        # empty batch
+    assert f(P, P, 1000, 4, 0, 1, 2, P, ws, None) == PA_ERR_SHAPE      # empty vocabulary
+    assert f(P, P, 996, 4, 1000, 1, 2, P, ws, None) == PA_ERR_SHAPE    # stride < vocab
+    assert f(P, P, 1000, 70000, 1000, 1, 2, P, ws, None) == PA_ERR_UNSUPPORTED
+    assert f(None, P, 1000, 4, 1000, 1, 2, P, ws, None) == PA_ERR_NULL
+    assert f(P, _fake(0x10002), 1000, 4, 1000, 1, 2, P, ws, None) == PA_ERR_UNSUPPORTED
+    assert f(P, P, 1000, 4, 1000, 1, 2, P, ws - 1, None) == PA_ERR_WORKSPACE
+    assert f(P, P, 1000, 4, 1000, 1, 2, None, ws, None) == PA_ERR_WORKSPACE
