@@ -212,6 +212,28 @@ int pa_bm_decode_metadata(const pa_block_manager* bm, const int64_t* seq_ids, in
                           int32_t* block_table, int32_t block_table_stride,
                           int32_t* max_context_len);
 
+/*
+ * How many KV blocks fit in device memory after a warm-up run.
+ * [Report] "nano-vllm 深度分析报告", section "创新之处" (the dynamic KV-cache
+ * sizing item) and table "可复用的模式与技巧", row "warmup → peak → 分配": run
+ * one warm-up step, record the allocator's peak, and budget
+ *     available = total * utilization - used - peak + current
+ * bytes, where -peak + current removes what the warm-up's temporaries took.
+ *   total_bytes    device memory size;
+ *   used_bytes     device memory in use now (total - free);
+ *   peak_bytes     the allocator's peak during the warm-up;
+ *   current_bytes  the allocator's current allocation after the warm-up;
+ *   utilization    fraction of the device to plan for (the pages use 0.9).
+ * One block holds K and V of block_size tokens for every layer:
+ *     block_bytes = 2 * num_layers * block_size * num_kv_heads * head_dim * dtype_bytes.
+ * Returns floor(available / block_bytes), 0 if available <= 0, or -1 on bad
+ * arguments (a size < 1, or utilization outside (0, 1]).
+ */
+int64_t pa_kv_cache_num_blocks(uint64_t total_bytes, uint64_t used_bytes, uint64_t peak_bytes,
+                               uint64_t current_bytes, double utilization, int32_t num_layers,
+                               int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t dtype_bytes);
+
 #ifdef __cplusplus
 }
 #endif

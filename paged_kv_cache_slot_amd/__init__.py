@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = ("pa_status_string", "pa_store_kvcache", "pa_decode_workspace
                     "pa_bm_can_append", "pa_bm_append", "pa_bm_append_batch", "pa_bm_deallocate", "pa_bm_seq_info",
                     "pa_bm_block_table", "pa_bm_block_info", "pa_bm_stats",
                     "pa_bm_batch_info", "pa_bm_prefill_metadata", "pa_bm_decode_metadata",
+                    "pa_kv_cache_num_blocks",
                     # sampler
                     "pa_sample_workspace_bytes", "pa_sample_gumbel",
                     # decode-step graphs

@@ -11,7 +11,8 @@ import numpy as np
 
 from . import PAError, library
 
-__all__ = ["BlockManager", "xxh64", "block_hash"]
+__all__ = ["BlockManager", "xxh64", "block_hash", "kv_cache_num_blocks",
+           "kv_cache_num_blocks_on_device"]
 
 _configured = False
 
@@ -41,6 +42,8 @@ def _lib():
             "pa_bm_batch_info": ([p, p, i32, p, p, p, p], ctypes.c_int),
             "pa_bm_prefill_metadata": ([p, p, i32, p, p, p, i32, p, i32, p, p], ctypes.c_int),
             "pa_bm_decode_metadata": ([p, p, i32, i32, p, p, p, i32, p], ctypes.c_int),
+            "pa_kv_cache_num_blocks": ([u64, u64, u64, u64, ctypes.c_double, i32, i32, i32, i32,
+                                        i32], i64),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(lib, name)
@@ -91,6 +94,31 @@ def block_hash(tokens, parent=None):
     t = _i32(tokens)
     return int(_lib().pa_block_hash(0 if parent is None else int(parent),
                                     0 if parent is None else 1, _ptr(t), len(t)))
+
+
+def kv_cache_num_blocks(total_bytes, used_bytes, peak_bytes, current_bytes, num_layers,
+                        block_size, num_kv_heads, head_dim, dtype_bytes=2, utilization=0.9):
+    """Blocks that fit in (total * utilization - used - peak + current) bytes
+    (pa_kv_cache_num_blocks)."""
+    n = _lib().pa_kv_cache_num_blocks(int(total_bytes), int(used_bytes), int(peak_bytes),
+                                      int(current_bytes), float(utilization), int(num_layers),
+                                      int(block_size), int(num_kv_heads), int(head_dim),
+                                      int(dtype_bytes))
+    if n < 0:
+        raise ValueError("pa_kv_cache_num_blocks: bad arguments")
+    return int(n)
+
+
+def kv_cache_num_blocks_on_device(num_layers, block_size, num_kv_heads, head_dim,
+                                  dtype_bytes=2, utilization=0.9, device=None):
+    """The same budget from the current device after a warm-up: total and free
+    memory from the runtime, peak and current from torch's allocator."""
+    import torch
+    free, total = torch.cuda.mem_get_info(device)
+    peak = torch.cuda.max_memory_allocated(device)
+    current = torch.cuda.memory_allocated(device)
+    return kv_cache_num_blocks(total, total - free, peak, current, num_layers, block_size,
+                               num_kv_heads, head_dim, dtype_bytes, utilization)
 
 
 class BlockManager:

@@ -586,4 +586,22 @@ int pa_bm_decode_metadata(const pa_block_manager* bm, const int64_t* seq_ids, in
   return PA_OK;
 }
 
+int64_t pa_kv_cache_num_blocks(uint64_t total_bytes, uint64_t used_bytes, uint64_t peak_bytes,
+                               uint64_t current_bytes, double utilization, int32_t num_layers,
+                               int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t dtype_bytes) {
+  if (!(utilization > 0.0 && utilization <= 1.0) || num_layers < 1 || block_size < 1 ||
+      num_kv_heads < 1 || head_dim < 1 || dtype_bytes < 1)
+    return -1;
+  // Exact in long double for any realistic device (64-bit mantissa).
+  const long double available = static_cast<long double>(total_bytes) * utilization -
+                                static_cast<long double>(used_bytes) -
+                                static_cast<long double>(peak_bytes) +
+                                static_cast<long double>(current_bytes);
+  const long double block_bytes = 2.0L * num_layers * block_size * num_kv_heads * head_dim *
+                                  dtype_bytes;
+  if (available <= 0.0L) return 0;
+  return static_cast<int64_t>(available / block_bytes);
+}
+
 }  // extern "C"

@@ -171,3 +171,30 @@ def test_manager_driven_prefill_decode_and_reuse():
     for step in range(3):
         say(f"[case] manager decode after reuse, step {step}")
         eng.decode_step([B, C, E, F], 4, rng)
+
+
+def test_kv_budget_on_device():
+    """After a warm-up, the budget from the device's own figures matches the
+    oracle on the same figures, and a KV cache of that many blocks (all 28
+    layers of a Qwen3-0.6B shape, at 5% of the device) can be allocated."""
+    import oracle.kv_budget as okb
+    from paged_kv_cache_slot_amd.block_manager import (kv_cache_num_blocks,
+                                                       kv_cache_num_blocks_on_device)
+    eng = Engine(seed=5)
+    eng.prefill({1: list(range(40))})                   # warm-up step
+    torch.cuda.synchronize()
+    free, total = torch.cuda.mem_get_info()
+    peak, cur = torch.cuda.max_memory_allocated(), torch.cuda.memory_allocated()
+    shape = dict(num_layers=28, block_size=256, num_kv_heads=8, head_dim=128)
+    n = kv_cache_num_blocks(total, total - free, peak, cur, utilization=0.05, **shape)
+    assert n == okb.num_blocks(total, total - free, peak, cur, 28, 256, 8, 128, 2, 0.05)
+    assert n > 0
+    n_dev = kv_cache_num_blocks_on_device(utilization=0.05, **shape)
+    assert abs(n_dev - n) <= 1 + n // 100             # the device figures move a little
+    block_bytes = 2 * 28 * 256 * 8 * 128 * 2
+    say(f"[case] kv budget: {n} blocks of {block_bytes} bytes at 5% of {total} bytes")
+    kv = torch.empty(n * block_bytes, dtype=torch.uint8, device=DEV)
+    kv[-1] = 1
+    torch.cuda.synchronize()
+    assert kv.numel() <= 0.05 * total
+    del kv
