@@ -397,6 +397,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-leg", choices=["prefill", "sampler"], default=None,
+                    help="only run this leg and print its own result (for counter runs under "
+                         "rocprofv3); the benchmark line is not printed")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (a known "
                          "byte count for scaling the HBM counters of rocprofv3)")
@@ -418,6 +421,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("[bench] copied 1 GiB 5 times")
+        return
+    if args.profile_leg:
+        fn = {"prefill": lambda: prefill_bench(args.warmup, args.steps),
+              "sampler": lambda: sampler_bench(args.warmup, args.steps)}[args.profile_leg]
+        res = fn()
+        print(json.dumps({k: v for k, v in res.items() if k != "case"}), flush=True)
         return
     log(f"device: {torch.cuda.get_device_name(0)} "
         f"({torch.cuda.get_device_properties(0).gcnArchName})")

@@ -182,21 +182,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int wave_pos0 = P + tok0 + (wave * 32) % TQ;    // lowest position of the wavefront's rows
   const int wave_pos1 = wave_pos0 + min(32, TQ) - 1;    // highest
 
-  // Q of this lane's row, pre-multiplied by scale * log2(e) and rounded to
-  // bf16 once, so the scores come out of the MFMA in log2 units.
-  bf16x8_t qreg[kHeadDim / 16];
+  // Q of this lane's row (loaded here, converted below once tile 0's copy is
+  // in flight too, so the two latencies overlap).
+  uint4 qraw[kHeadDim / 16];
+  bf16x8_t qreg[kHeadDim / 16];  // filled once tile 0 is requested
   {
     const uint16_t* qp = q + (static_cast<int64_t>(qt) * num_q_heads + head) * kHeadDim + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qp + ks * 16);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      uint32_t sw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sw[i] = pack_bf16x2(bf16_lo(w[i]) * scale_log2, bf16_hi(w[i]) * scale_log2);
-      qreg[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(sw[0], sw[1], sw[2], sw[3]));
-    }
+    for (int ks = 0; ks < kHeadDim / 16; ++ks)
+      qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 16);
   }
 
   f32x16_t o[kHeadDim / 32];
@@ -446,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   // ---- pipeline ------------------------------------------------------------
   // One step: tile t is in (kc, vc); tile t+1 goes into (kn, vn). Block ids
   // are fetched one step ahead of their DMA.
-  int blk_next = block_of(1);
+  int blk_next = 0;  // block ids of the next tile's copy, fetched one step ahead
   auto step = [&](int t, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     // Tile t has landed (this wavefront's copies), then everyone's have, and
     // everyone is done with the stage that tile t+1 will overwrite.
@@ -459,6 +453,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     blk_next = block_of(t + 2);
   };
   issue_tile(0, block_of(0), lds_k0, lds_v0);
+  blk_next = block_of(1);
+
+  // Q pre-multiplied by scale * log2(e) and rounded to bf16 once, so the
+  // scores come out of the MFMA in log2 units.
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+    const uint32_t w[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+    uint32_t sw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sw[i] = pack_bf16x2(bf16_lo(w[i]) * scale_log2, bf16_hi(w[i]) * scale_log2);
+    qreg[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(sw[0], sw[1], sw[2], sw[3]));
+  }
+
   for (int t = 0; t < num_tiles; t += 2) {
     step(t, lds_k0, lds_v0, lds_k1, lds_v1);
     if (t + 1 < num_tiles) step(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
