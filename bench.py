@@ -436,7 +436,7 @@ def main():
     case = main_res["case"]
     digest = source_digest("decode.hip", "pa_internal.h")
     traffic = measured_traffic("pa_decode", digest)
-    roofline = {"kernel": "pa_decode (decode_kernel<2, 4> + decode_reduce_kernel)",
+    roofline = {"kernel": "pa_decode (decode_kernel<2, 4> + decode_merge_kernel<2>)",
                 "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),

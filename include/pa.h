@@ -91,8 +91,12 @@ int pa_store_kvcache(const void* k, const void* v, int64_t kv_token_stride,
                      int32_t num_kv_heads, int32_t head_dim, void* stream);
 
 /*
- * Bytes of device workspace pa_decode needs for these sizes (the split-K
- * partial results). 0 is never returned for a valid call with batch > 0.
+ * Bytes of device workspace pa_decode needs for these sizes: a small header,
+ * then per working wavefront its first pair and two partial (acc, max, sum)
+ * records per query head, for the pairs its range of the work cuts. The bound
+ * depends on min(batch, 1024) (longer batches run in consecutive launches
+ * that reuse the workspace), num_q_heads and max_context_len only; block_size
+ * and head_dim are accepted for symmetry. 0 only for batch <= 0.
  */
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                  int32_t head_dim, int32_t max_context_len,

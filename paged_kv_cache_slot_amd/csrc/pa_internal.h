@@ -12,9 +12,6 @@ namespace pa {
 // token, i.e. sixteen 16-byte vectors.
 constexpr int kHeadDim = 128;
 
-// Decode splits each context into pieces of this many tokens; one work-group
-// handles one (sequence, kv head, piece).
-constexpr int kDecodeSplit = 256;
 
 // Devices whose per-device launch data (occupancy, symbol addresses) is cached.
 constexpr int kMaxDevices = 64;
