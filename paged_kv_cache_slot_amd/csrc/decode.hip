@@ -47,7 +47,7 @@ namespace {
 
 constexpr int kScanRows = 1024;        // sequences per launch (their lengths sit in LDS)
 constexpr int kPairCost = 2;           // per-(sequence, kv head) overhead, in chunk units
-constexpr int kMinUnits = 32;          // fewest cost units a wavefront is given
+constexpr int kMinUnits = 16;          // fewest cost units a wavefront is given
 constexpr float kLazyLog2 = 8.f;       // headroom of the softmax reference (log2 units)
 constexpr int kRecord = 132;           // floats per partial record: acc[128], max, sum, pad
 constexpr int kInfoOffset = 64;        // workspace bytes before the per-wavefront records
@@ -574,8 +574,16 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                  int32_t num_kv_heads, int32_t log2_bs, int32_t max_context_len, float scale_log2,
                  char* workspace, hipStream_t stream, hipError_t* err) {
   constexpr int W = decode_waves<G>();
-  const int groups = resident_groups<G, CH>();
   const int nb = std::min(batch, kScanRows);
+  // No more work-groups than the most work these rows can hold needs (the
+  // kernel gives a wavefront at least kMinUnits units): small batches then do
+  // not start a work-group per CU only to scan context_lens and leave.
+  const int64_t max_units =
+      static_cast<int64_t>(nb) * num_kv_heads *
+      ((std::max(0, max_context_len) + 4 * CH - 1) / (4 * CH) + kPairCost);
+  const int groups = static_cast<int>(std::max<int64_t>(
+      1, std::min<int64_t>(resident_groups<G, CH>(),
+                           (max_units + kMinUnits * W - 1) / (kMinUnits * W))));
   hipLaunchKernelGGL((decode_kernel<G, CH>), dim3(static_cast<uint32_t>(groups)), dim3(64 * W),
                      0, stream, out, q, k_cache, v_cache, block_table, bt_stride, context_lens,
                      nb, num_q_heads, num_kv_heads, log2_bs, max_context_len, scale_log2,
