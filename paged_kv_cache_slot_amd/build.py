@@ -4,11 +4,6 @@ Every HIP source is compiled with packed-fp32 code generation switched off
 (`-Xclang -target-feature -Xclang -packed-fp32-ops`); hipcc's host pass warns
 that it does not know that feature, which is harmless.
 
-LLVM's atomic optimizer is switched off: the decode kernel's only atomics are
-one-lane fetches of a work-group's LDS work counter whose result is needed a
-whole item later, and the optimizer's wave-wide rewrite reads the result back
-at once, which waits for every load in flight.
-
 Host-only C++ sources (the block manager) are compiled by the host compiler
 and linked into the same library; `bm_bench`, the block manager's host
 benchmark executable, is linked from the same object.
@@ -34,7 +29,6 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
