@@ -51,12 +51,15 @@ constexpr int kMinUnits = 16;          // fewest cost units a wavefront is given
 constexpr float kLazyLog2 = 8.f;       // headroom of the softmax reference (log2 units)
 constexpr int kRecord = 132;           // floats per partial record: acc[128], max, sum, pad
 constexpr int kInfoOffset = 64;        // workspace bytes before the per-wavefront records
+constexpr int kMergeWaves = 16;        // wavefronts per work-group of the merge
 
 // Workspace layout. Header (int64): the total cost C and the number of working
-// wavefronts nw. Then per wavefront w < nw, four int64: the pair holding w's
-// first unit (sequence, kv head) and that pair's units [P0, P1). Then per
-// wavefront two partial slots (0: its first pair, 1: its last pair), each G
-// records of kRecord floats, one per query head of the pair.
+// wavefronts nw. Then per wavefront w < nw, the merge job of the range
+// boundary at w's first unit, four int64: sequence, kv head, the first
+// wavefront w_a holding a piece of that pair, and (pieces | slot of w_a's
+// piece << 32), with 0 pieces where w is not the last boundary cutting the
+// pair. Then per wavefront two partial slots (0: its first pair, 1: its last
+// pair), each G records of kRecord floats, one per query head of the pair.
 __host__ __device__ constexpr size_t partial_offset(int64_t nw) {
   return kInfoOffset + static_cast<size_t>(nw) * 4 * sizeof(int64_t);
 }
@@ -193,10 +196,21 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
     started = 0;
     pair_c0 = 0;
     if (lane == 0) {
+      // The boundary at lo merges its pair when it cuts the pair's chunks and
+      // no later boundary does. Pieces of wavefronts after w_a start with the
+      // pair (slot 0); w_a's piece is its last pair unless the pair began
+      // where its range begins.
+      const int64_t P1 = P0 + wn + kPairCost;
+      int64_t wa = 0, job = 0;
+      if (P0 + kPairCost < lo && lo < P1 && hi >= P1) {
+        wa = ((P0 + kPairCost + 1) * nw - 1) / C;
+        const int64_t slot_wa = C * wa / nw >= P0 ? 0 : 1;
+        job = (gw - wa + 1) | (slot_wa << 32);
+      }
       info[4 * gw + 0] = wb;
       info[4 * gw + 1] = wg;
-      info[4 * gw + 2] = P0;
-      info[4 * gw + 3] = P0 + wn + kPairCost;
+      info[4 * gw + 2] = wa;
+      info[4 * gw + 3] = job;
     }
   }
   auto advance = [&]() {
@@ -487,57 +501,75 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   }
 }
 
-// Merges the pieces of pairs cut by range boundaries. One wavefront per
-// boundary w (the first unit of wavefront w's range) and four per work-group;
-// the boundary's pair is merged here when w is its last cut, from the partial
-// slots of wavefronts w_a .. w (w_a holds the pair's first chunk; wavefront x
-// wrote its part in slot 0 when the pair is its first pair, else in slot 1).
-// Each lane handles two elements of head_dim for every query head.
+// Merges the pieces of pairs cut by range boundaries: one wavefront per
+// boundary w, kMergeWaves per work-group, working on the job wavefront w
+// recorded.
+// The job and the header are read together (an entry past nw is stale but
+// inside the workspace, and is ignored); the pieces are then read four at a
+// time, all loads in flight together, and folded in order with the online
+// (max, sum, acc) rescaling. Each lane handles two elements of head_dim for
+// every query head.
 template <int G>
-__global__ __launch_bounds__(256) void decode_merge_kernel(uint16_t* __restrict__ out,
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(uint16_t* __restrict__ out,
                                                            int32_t num_q_heads,
                                                            const char* __restrict__ ws) {
-  const int64_t* hdr = reinterpret_cast<const int64_t*>(ws);
-  const int64_t C = hdr[0], nw = hdr[1];
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (w < 1 || w >= nw) return;
-  const int64_t* info = reinterpret_cast<const int64_t*>(ws + kInfoOffset) + 4 * w;
-  const int b = static_cast<int>(info[0]), g = static_cast<int>(info[1]);
-  const int64_t P0 = info[2], P1 = info[3];
-  const int64_t lo = C * w / nw, lo_next = C * (w + 1) / nw;
-  if (!(P0 + kPairCost < lo && lo < P1)) return;  // the boundary does not cut a chunk run
-  if (lo_next < P1) return;                       // a later boundary also cuts this pair
-  const int64_t wa = ((P0 + kPairCost + 1) * nw - 1) / C;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
+  const int64_t nw = reinterpret_cast<const int64_t*>(ws)[1];
+  const int64_t* job = reinterpret_cast<const int64_t*>(ws + kInfoOffset) + 4 * w;
+  const int64_t b = job[0], g = job[1], wa = job[2], pj = job[3];
+  if (w >= nw) return;
+  const int np = static_cast<int>(pj & 0xffffffff);
+  if (np == 0) return;
+  const int slot_wa = static_cast<int>(pj >> 32);
   const float* part = reinterpret_cast<const float*>(ws + partial_offset(nw));
   const int d = (threadIdx.x & 63) * 2;
-  // One pass over the pair's pieces in order, online max and sum per query head.
   float M[G], o0[G], o1[G], lt[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     M[hh] = -INFINITY;
     o0[hh] = o1[hh] = lt[hh] = 0.f;
   }
-  for (int64_t x = wa; x <= w; ++x) {
-    const int slot = C * x / nw >= P0 ? 0 : 1;
+  constexpr int kU = 4;
+  for (int x0 = 0; x0 < np; x0 += kU) {
+    float mx[kU][G], lx[kU][G];
+    float2 vx[kU][G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float* rec = part + ((x * 2 + slot) * G + hh) * kRecord;
-      const float mx = rec[kHeadDim];
-      const float mn = fmaxf(M[hh], mx);
-      const float a = fast_exp2(M[hh] - mn);  // 0 while M is -inf
-      const float c = fast_exp2(mx - mn);
-      const float2 v = *reinterpret_cast<const float2*>(rec + d);
-      o0[hh] = o0[hh] * a + c * v.x;
-      o1[hh] = o1[hh] * a + c * v.y;
-      lt[hh] = lt[hh] * a + c * rec[kHeadDim + 1];
-      M[hh] = mn;
+    for (int u = 0; u < kU; ++u) {
+      const int x = x0 + u;
+      const int slot = x == 0 ? slot_wa : 0;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        if (x < np) {
+          const float* rec = part + (((wa + x) * 2 + slot) * G + hh) * kRecord;
+          mx[u][hh] = rec[kHeadDim];
+          lx[u][hh] = rec[kHeadDim + 1];
+          vx[u][hh] = *reinterpret_cast<const float2*>(rec + d);
+        } else {
+          mx[u][hh] = -INFINITY;
+          lx[u][hh] = 0.f;
+          vx[u][hh] = make_float2(0.f, 0.f);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float mn = fmaxf(M[hh], mx[u][hh]);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float a = fast_exp2(M[hh] - mu);  // 0 while M is -inf
+        const float c = fast_exp2(mx[u][hh] - mu);
+        o0[hh] = o0[hh] * a + c * vx[u][hh].x;
+        o1[hh] = o1[hh] * a + c * vx[u][hh].y;
+        lt[hh] = lt[hh] * a + c * lx[u][hh];
+        M[hh] = mn;
+      }
     }
   }
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const float inv = 1.f / lt[hh];
-    *reinterpret_cast<uint32_t*>(
-        out + (static_cast<int64_t>(b) * num_q_heads + g * G + hh) * kHeadDim + d) =
+    *reinterpret_cast<uint32_t*>(out + (b * num_q_heads + g * G + hh) * kHeadDim + d) =
         pack_bf16x2(o0[hh] * inv, o1[hh] * inv);
   }
 }
@@ -590,9 +622,9 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                      workspace, 0);
   *err = hipGetLastError();
   if (*err == hipSuccess) {
-    const int merge_groups = (groups * W + 3) / 4;
+    const int merge_groups = (groups * W + kMergeWaves - 1) / kMergeWaves;
     hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(static_cast<uint32_t>(merge_groups)),
-                       dim3(256), 0, stream, out, num_q_heads,
+                       dim3(64 * kMergeWaves), 0, stream, out, num_q_heads,
                        static_cast<const char*>(workspace));
     *err = hipGetLastError();
   }
