@@ -142,12 +142,26 @@ def decode_bench(name, warmup, steps):
             ev[1].record()
 
     ms, kms = run_timed(step, warmup, steps)
+    # The same call again with the 256 MB last-level cache (MALL) overwritten
+    # before each one (a 512 MiB fill outside the timed events), so that no
+    # part of the pool can be served from it: median of the decode calls.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    evs = []
+    for i in range(steps):
+        scratch.fill_(i & 0xFF)
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        step(i, ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    flushed_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del scratch
     dbytes = decode_bytes(case)
     sbytes = store_bytes(case)
     kern_ms = float(np.mean(kms))
     res = dict(case=case, ms_per_step=ms, step_bytes=dbytes + sbytes, decode_bytes=dbytes,
                decode_ms=kern_ms, gbs=(dbytes + sbytes) / (ms * 1e-3) / 1e9,
-               decode_gbs=dbytes / (kern_ms * 1e-3) / 1e9)
+               decode_gbs=dbytes / (kern_ms * 1e-3) / 1e9, flushed_ms=flushed_ms,
+               flushed_gbs=dbytes / (flushed_ms * 1e-3) / 1e9)
     return res
 
 
@@ -442,6 +456,8 @@ def main():
                 "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": main_res["decode_bytes"],
                 "avg_launch_us": round(main_res["decode_ms"] * 1e3, 2),
+                "mall_flushed_median_us": round(main_res["flushed_ms"] * 1e3, 2),
+                "mall_flushed_frac": round(main_res["flushed_gbs"] / HBM_PEAK_GBS, 4),
                 "source_digest": digest}
 
     secondary = []
@@ -454,7 +470,9 @@ def main():
                 "step_GBps": round(r["gbs"], 2),
                 "decode_us": round(r["decode_ms"] * 1e3, 2),
                 "decode_GBps": round(r["decode_gbs"], 2),
-                "decode_frac_hbm": round(r["decode_gbs"] / HBM_PEAK_GBS, 4)})
+                "decode_frac_hbm": round(r["decode_gbs"] / HBM_PEAK_GBS, 4),
+                "mall_flushed_median_us": round(r["flushed_ms"] * 1e3, 2),
+                "mall_flushed_frac": round(r["flushed_gbs"] / HBM_PEAK_GBS, 4)})
             del r
             torch.cuda.empty_cache()
         log("[bench] qwen3_8b_prefill_prefix: store + prefill")
