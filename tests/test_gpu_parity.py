@@ -116,7 +116,8 @@ DECODE_GRID = [
 @pytest.mark.parametrize("bs,hq,hkv,lens", DECODE_GRID,
                          ids=[f"bs{a}-hq{b}-hkv{c}" for a, b, c, _ in DECODE_GRID])
 def test_decode_grid_all_rows(bs, hq, hkv, lens):
-    """Several pieces, ragged tails, padding rows, every GQA ratio."""
+    """Pairs cut by the work split, ragged chunk and block tails, padding rows,
+    every GQA ratio."""
     say(f"[case] decode grid bs={bs} Hq={hq} Hkv={hkv} lens={lens}")
     case = workloads.decode_case(len(lens), (1, 2048), hq, hkv, 128, bs, seed=77 + bs + hq,
                                  device=DEV, lens=lens, spare_blocks=5)
@@ -134,8 +135,9 @@ def test_decode_grid_all_rows(bs, hq, hkv, lens):
 
 
 def test_decode_large_batch_long_pieces():
-    """520 rows x 8 kv heads (more than 4096 pairs, so pieces of 1024 tokens),
-    lengths on and around the piece boundaries, padding rows: every row."""
+    """520 rows x 8 kv heads (4160 pairs, most of them cut between wavefronts),
+    lengths on and around chunk, block and 1024-token boundaries, padding rows:
+    every row."""
     rng = np.random.default_rng(41)
     lens = rng.integers(1, 2100, size=520)
     lens[:12] = [1, 1023, 1024, 1025, 2047, 2048, 2049, 0, 511, 512, 513, 2099]
@@ -174,7 +176,8 @@ def test_decode_more_rows_than_one_scan_window():
 
 
 def test_decode_max_context_len_above_all_rows():
-    """A loose max_context_len (more pieces than any row needs) changes nothing."""
+    """A loose max_context_len (a larger workspace bound and grid cap than the rows
+    need) changes neither the work split nor any output bit."""
     lens = [40, 300, 0, 513]
     case = workloads.decode_case(4, (1, 2048), 16, 8, 128, 16, seed=3, device=DEV, lens=lens)
     tight = gpu_decode(case)
