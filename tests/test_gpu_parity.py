@@ -155,6 +155,35 @@ def test_decode_large_batch_long_pieces():
     assert int(out[7].float().abs().sum()) == 0
 
 
+LONG_ROWS = [
+    # (block_size, Hq, Hkv, lengths)
+    (256, 16, 8, [40000, 5, 0, 3000]),
+    (128, 32, 8, [25000, 1]),
+    (64, 8, 8, [12345]),
+]
+
+
+@pytest.mark.parametrize("bs,hq,hkv,lens", LONG_ROWS,
+                         ids=[f"bs{a}-hq{b}-hkv{c}" for a, b, c, _ in LONG_ROWS])
+def test_decode_long_rows_many_pieces(bs, hq, hkv, lens):
+    """Few very long rows: each (sequence, kv head) pair is cut between tens to
+    hundreds of wavefronts, so the merge folds many pieces per pair."""
+    say(f"[case] decode long rows bs={bs} Hq={hq} Hkv={hkv} lens={lens}")
+    case = workloads.decode_case(len(lens), (1, 2048), hq, hkv, 128, bs, seed=5 + bs,
+                                 device=DEV, lens=lens, spare_blocks=2)
+    h = host_copy(case)
+    gpu_store(case)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
+                        nthreads=ORACLE_THREADS)
+    compare(out, ref, "decode long rows")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert int(out[b].float().abs().sum()) == 0
+
+
 def test_decode_more_rows_than_one_scan_window():
     """2600 rows (more than the 1024 rows of context lengths a work-group holds in
     LDS at once), mixed lengths and padding: every row against the oracle."""
