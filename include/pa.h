@@ -92,8 +92,9 @@ int pa_store_kvcache(const void* k, const void* v, int64_t kv_token_stride,
 
 /*
  * Bytes of device workspace pa_decode needs for these sizes: a small header,
- * then per working wavefront its first pair and two partial (acc, max, sum)
- * records per query head, for the pairs its range of the work cuts. The bound
+ * then per working wavefront the merge job of the boundary where its range of
+ * the work starts, and two partial (acc, max, sum) records per query head,
+ * for the (sequence, kv head) pairs its range cuts. The bound
  * depends on min(batch, 1024) (longer batches run in consecutive launches
  * that reuse the workspace), num_q_heads and max_context_len only; block_size
  * and head_dim are accepted for symmetry. 0 only for batch <= 0.
