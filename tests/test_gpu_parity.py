@@ -305,6 +305,34 @@ def test_prefill_grid_all_rows(bs, hq, hkv, new, pre):
     compare(out, ref, "prefill grid")
 
 
+def test_prefill_sequences_without_new_tokens():
+    """Batch members with no new tokens (N = 0, cached prefix only) contribute no
+    rows and leave their neighbours' rows exact; a batch with no new token at
+    all is a no-op."""
+    new, pre = [0, 50, 0, 3, 0], [2, 1, 0, 3, 3]
+    say(f"[case] prefill with empty sequences new={new} prefix_blocks={pre}")
+    case = workloads.prefill_case(len(new), (1, 64), 32, 8, 128, 16, seed=71, device=DEV,
+                                  chains=2, chain_blocks=3, new_lens=new, prefix_blocks=pre,
+                                  prefix_chain=[0, 1, 0, 1, 1])
+    h = host_copy(case)
+    gpu_store(case)
+    out = gpu_prefill(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    ref = oracle.prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["context_lens"], h["block_table"],
+                         h["scale"], nthreads=ORACLE_THREADS)
+    assert out.shape[0] == 53
+    compare(out, ref, "prefill with empty sequences")
+    empty = workloads.prefill_case(3, (1, 64), 32, 8, 128, 16, seed=72, device=DEV, chains=2,
+                                   chain_blocks=3, new_lens=[0, 0, 0], prefix_blocks=[1, 2, 0],
+                                   prefix_chain=[0, 1, 0])
+    assert empty["q"].shape[0] == 0
+    gpu_store(empty)
+    out = gpu_prefill(empty)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+
+
 def test_prefill_row_matches_gpu_decode():
     """Prefill row i of a sequence with prefix P equals decode with L = P + i + 1."""
     case = workloads.prefill_case(1, (1, 1024), 32, 8, 128, 16, seed=61, device=DEV, chains=1,
