@@ -103,18 +103,30 @@ def prefill_flops(case):
 
 def run_timed(step, warmup, steps):
     """Warm up, then time exactly `steps` calls of step(i) between two device
-    synchronisations. Returns (ms per step, [per-step kernel ms])."""
+    synchronisations. Returns (ms per step, [per-step kernel ms]). Python's
+    garbage collector is paused (not run) from the warm-up to the end of the
+    timed steps: a full collection can stall the launching thread for tens of
+    milliseconds, and the GPU idle it causes lowers its clocks (measured: a
+    50 ms idle gap before the warm-up slows the next Qwen3-8B decode steps by
+    about 10%)."""
+    import gc
     import torch
-    for i in range(warmup):
-        step(i, None)
-    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    was_enabled = gc.isenabled()
+    gc.disable()
+    try:
+        for i in range(warmup):
+            step(i, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+    finally:
+        if was_enabled:
+            gc.enable()
     return ms, [a.elapsed_time(b) for a, b in evs]
 
 
@@ -161,6 +173,8 @@ def decode_bench(name, warmup, steps):
     res = dict(case=case, ms_per_step=ms, step_bytes=dbytes + sbytes, decode_bytes=dbytes,
                decode_ms=kern_ms, gbs=(dbytes + sbytes) / (ms * 1e-3) / 1e9,
                decode_gbs=dbytes / (kern_ms * 1e-3) / 1e9, flushed_ms=flushed_ms,
+               decode_ms_min=float(np.min(kms)), decode_ms_median=float(np.median(kms)),
+               decode_ms_max=float(np.max(kms)),
                flushed_gbs=dbytes / (flushed_ms * 1e-3) / 1e9)
     return res
 
