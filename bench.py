@@ -83,11 +83,12 @@ def decode_bytes(case):
     return kv + q + out
 
 
-def store_bytes(case):
-    """Read k and v of every live new token, write them into the pools."""
-    import torch
+def store_bytes(case, fused=False):
+    """pa_store_kvcache: read k and v of every stored new token, write them into
+    the pools. Fused into the decode (pa_decode_store), the read is the decode's
+    own read of the new token (already in decode_bytes): only the writes."""
     live = int((case["slot_mapping"] >= 0).sum())
-    return live * case["num_kv_heads"] * case["head_dim"] * 2 * 2 * 2
+    return live * case["num_kv_heads"] * case["head_dim"] * 2 * 2 * (1 if fused else 2)
 
 
 def prefill_flops(case):
@@ -130,7 +131,7 @@ def run_timed(step, warmup, steps):
     return ms, [a.elapsed_time(b) for a, b in evs]
 
 
-def decode_bench(name, warmup, steps):
+def decode_bench(name, warmup, steps, fused=True):
     import torch
     import numpy as np
     import paged_kv_cache_slot_amd as pa
@@ -144,6 +145,15 @@ def decode_bench(name, warmup, steps):
     torch.cuda.synchronize()
 
     def step(i, ev):
+        if fused:  # the store fused into the decode launch
+            if ev:
+                ev[0].record()
+            pa.pa_decode_store(out, case["q"], case["k_new"], case["v_new"], case["k_cache"],
+                               case["v_cache"], case["slot_mapping"], case["block_table"],
+                               case["context_lens"], case["max_context_len"], case["scale"], ws)
+            if ev:
+                ev[1].record()
+            return
         pa.pa_store_kvcache(case["k_new"], case["v_new"], case["k_cache"], case["v_cache"],
                             case["slot_mapping"])
         if ev:
@@ -167,8 +177,9 @@ def decode_bench(name, warmup, steps):
     torch.cuda.synchronize()
     flushed_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
     del scratch
-    dbytes = decode_bytes(case)
-    sbytes = store_bytes(case)
+    # Bytes of the timed call: the decode's, plus the fused store's writes.
+    dbytes = decode_bytes(case) + (store_bytes(case, fused=True) if fused else 0)
+    sbytes = 0 if fused else store_bytes(case)
     kern_ms = float(np.mean(kms))
     res = dict(case=case, ms_per_step=ms, step_bytes=dbytes + sbytes, decode_bytes=dbytes,
                decode_ms=kern_ms, gbs=(dbytes + sbytes) / (ms * 1e-3) / 1e9,
@@ -273,8 +284,8 @@ def graph_bench(batches=(1, 4, 16, 64, 256), steps=200, warmup=10):
     eagerly, per batch size, on the Qwen3-0.6B decode shape (16 q / 8 kv
     heads, block_size 256, context lengths U[100,2048], permuted blocks).
     Both paths are driven from Python the way a serving loop would: eager =
-    pa_store_kvcache + pa_decode per step, graph = one pa_decode_graphs_launch
-    per step. Two patterns, wall-clock microseconds per step over `steps`
+    one pa_decode_store call per step (its two kernel launches), graph = one
+    pa_decode_graphs_launch per step (the same launches captured). Two patterns, wall-clock microseconds per step over `steps`
     steps: dependent (the host waits for every step, as a decode loop that
     samples from each step must) and pipelined (steps enqueued back to back,
     one wait at the end)."""
@@ -317,9 +328,8 @@ def graph_bench(batches=(1, 4, 16, 64, 256), steps=200, warmup=10):
         table[:bucket].copy_(torch.from_numpy(t))
 
         def eager():
-            pa.pa_store_kvcache(kn[:batch], vn[:batch], kc, vc, slots[:batch])
-            pa.pa_decode(out[:batch], q[:batch], kc, vc, table[:batch], lens[:batch], max_len,
-                         scale, ws)
+            pa.pa_decode_store(out[:batch], q[:batch], kn[:batch], vn[:batch], kc, vc,
+                               slots[:batch], table[:batch], lens[:batch], max_len, scale, ws)
 
         def graph():
             graphs.launch(batch)
@@ -459,12 +469,13 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)} "
         f"({torch.cuda.get_device_properties(0).gcnArchName})")
 
-    log("[bench] qwen3_0.6b_decode: store + decode")
+    log("[bench] qwen3_0.6b_decode: decode step (store fused into decode)")
     main_res = decode_bench("qwen3_0.6b_decode", args.warmup, args.steps)
     case = main_res["case"]
     digest = source_digest("decode.hip", "pa_internal.h")
-    traffic = measured_traffic("pa_decode", digest)
-    roofline = {"kernel": "pa_decode (decode_kernel<2, 4> + decode_merge_kernel<2>)",
+    traffic = measured_traffic("pa_decode_store", digest)
+    roofline = {"kernel": "pa_decode_store (decode_kernel<2, 4> with the store fused, "
+                          "+ decode_merge_kernel<2>)",
                 "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
@@ -477,7 +488,7 @@ def main():
     secondary = []
     if not args.no_secondary:
         for name in ("qwen3_8b_decode", "bs16_stress_decode"):
-            log(f"[bench] {name}: store + decode")
+            log(f"[bench] {name}: decode step (store fused into decode)")
             r = decode_bench(name, args.warmup, args.steps)
             secondary.append({
                 "workload": name, "ms_per_step": round(r["ms_per_step"], 4),
@@ -521,7 +532,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(main_res["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "qwen3_0.6b_decode: pa_store_kvcache + pa_decode, 256 sequences, "
+        "config": {"workload": "qwen3_0.6b_decode: pa_decode_store (the new tokens' K/V store "
+                               "fused into the decode), 256 sequences, "
                                "context lengths U[100,2048], 16 q / 8 kv heads, head_dim 128, "
                                "block_size 256, permuted physical blocks",
                    "batch": case["batch"], "max_context_len": case["max_context_len"],

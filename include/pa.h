@@ -138,6 +138,40 @@ int pa_decode(void* out, const void* q, const void* k_cache,
               void* stream);
 
 /*
+ * pa_decode_store -- the decode step in one call: pa_store_kvcache of the
+ * step's new tokens fused into pa_decode (one decode launch and its merge
+ * instead of a separate store launch before them).
+ * [Report] "nano-vllm 深度分析报告", table "可复用的模式与技巧" (the store
+ * of each step's K/V through slot_mapping, -1 skipped); [QbitAI], section
+ * "vLLM是什么？" (block-table addressed KV blocks).
+ *
+ *   Same result, bit for bit (output and pools), as
+ *     pa_store_kvcache(k_new, v_new, kv_token_stride, k_cache, v_cache,
+ *                      slot_mapping, batch, num_blocks, block_size, ...);
+ *     pa_decode(out, q, k_cache, v_cache, block_table, ..., context_lens, ...);
+ *   under the decode-step layout of slot_mapping: for a live row
+ *   (context_lens[b] > 0) slot_mapping[b] is the slot of its position
+ *   context_lens[b] - 1 (the new token), or -1 when that token is already in
+ *   the pool; for a padding row (context_lens[b] == 0) it is -1. Other
+ *   layouts are undefined (the separate calls handle any slot_mapping).
+ *   The wavefront that holds a (sequence, kv head)'s last chunk reads the new
+ *   token from k_new/v_new and writes it into its slot; nothing else in the
+ *   call reads that slot.
+ *
+ *   k_new, v_new  [batch][kv_token_stride] bf16, first num_kv_heads*head_dim
+ *                 used; kv_token_stride a multiple of 8.
+ *   k_cache, v_cache are read and written; the other arguments, the workspace
+ *   and the errors are as for pa_store_kvcache and pa_decode.
+ */
+int pa_decode_store(void* out, const void* q, const void* k_new, const void* v_new,
+                    int64_t kv_token_stride, void* k_cache, void* v_cache,
+                    const int32_t* slot_mapping, const int32_t* block_table,
+                    int32_t block_table_stride, const int32_t* context_lens, int32_t batch,
+                    int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_context_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_varlen -- causal attention for a batch of variable-length
  * prompts whose leading blocks may come from the prefix cache.
  * [QbitAI] "vLLM是什么？" (paging) and [Report] "创新之处" (prefix caching).
@@ -225,8 +259,9 @@ int pa_sample_gumbel(int32_t* tokens, const float* probs, int64_t row_stride, in
 
 /*
  * Decode-step graphs: one HIP graph per batch-size bucket, each holding a
- * whole decode step (pa_store_kvcache of the step's new tokens, then
- * pa_decode) captured once and replayed with a single launch.
+ * whole decode step (the launches of pa_decode_store: the step's store fused
+ * into the decode kernel, then the merge) captured once and replayed with a
+ * single launch.
  * [Report] "nano-vllm 深度分析报告", section "创新之处" (graph capture at a
  * few batch sizes only, a batch rounded up to the next captured size, captured
  * from the largest size down with one memory pool shared by all graphs) and
@@ -240,6 +275,9 @@ int pa_sample_gumbel(int32_t* tokens, const float* probs, int64_t row_stride, in
  * with rows past `batch` as padding: context length 0 and slot -1 (what
  * pa_bm_decode_metadata writes for padded_batch = bucket); their q, k_new and
  * v_new rows may hold anything finite and their output rows come back zero.
+ * A live row's slot is the slot of its new token (position context_lens[b]
+ * - 1) or -1, the layout pa_decode_store requires (pa_bm_decode_metadata
+ * writes it).
  * Rows [0, bucket) of `out` are written. Every context length of a replay
  * must be <= max_context_len given at creation.
  */

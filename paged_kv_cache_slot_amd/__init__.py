@@ -21,7 +21,7 @@ mappings, lengths) with chained-hash prefix caching is bound in
 import ctypes
 import os
 
-__all__ = ["PAError", "library", "lib_path", "pa_store_kvcache", "pa_decode",
+__all__ = ["PAError", "library", "lib_path", "pa_store_kvcache", "pa_decode", "pa_decode_store",
            "pa_decode_workspace_bytes", "pa_prefill_varlen", "pa_validate_metadata",
            "pa_status_string", "pa_sample_workspace_bytes", "pa_sample_gumbel",
            "pa_decode_graphs_create", "DecodeGraphs", "DEFAULT_BUCKETS",
@@ -31,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ("pa_status_string", "pa_store_kvcache", "pa_decode_workspace_bytes",
-                    "pa_decode", "pa_prefill_varlen", "pa_validate_metadata",
+                    "pa_decode", "pa_decode_store", "pa_prefill_varlen", "pa_validate_metadata",
                     # block manager (include/pa_block_manager.h, block_manager.py)
                     "pa_xxh64", "pa_block_hash", "pa_bm_create", "pa_bm_destroy",
                     "pa_bm_num_free_blocks", "pa_bm_can_allocate", "pa_bm_allocate",
@@ -89,6 +89,9 @@ def library():
         lib.pa_decode.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i32,
                                   ctypes.c_float, p, sz, p]
         lib.pa_decode.restype = ctypes.c_int
+        lib.pa_decode_store.argtypes = [p, p, p, p, i64, p, p, p, p, i32, p, i32, i32, i32,
+                                        i32, i32, i32, i32, ctypes.c_float, p, sz, p]
+        lib.pa_decode_store.restype = ctypes.c_int
         lib.pa_prefill_varlen.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                           i32, i32, ctypes.c_float, p]
         lib.pa_prefill_varlen.restype = ctypes.c_int
@@ -195,6 +198,39 @@ def pa_decode(out, q, k_cache, v_cache, block_table, context_lens, max_context_l
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream))
     _check("pa_decode", rc)
+
+
+def pa_decode_store(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_table,
+                    context_lens, max_context_len, scale, workspace, stream=None):
+    """The decode step in one call: pa_store_kvcache(k_new, v_new, ..., slot_mapping)
+    fused into pa_decode. k_new, v_new: [B, Hkv, D] or [B, >= Hkv*D] bf16 rows;
+    slot_mapping [B] int32 in the decode-step layout (a live row's new-token slot or
+    -1; -1 for padding rows); the rest as for pa_decode."""
+    import torch
+    num_blocks, bs, hkv, d = _pool_shape(k_cache, v_cache)
+    B, hq, dq = (int(x) for x in q.shape)
+    if out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("out and q must be contiguous [B, Hq, D]")
+    if not block_table.is_contiguous() or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be a contiguous [B, stride] int32 tensor")
+    k2 = k_new.flatten(1) if k_new.dim() == 3 else k_new
+    v2 = v_new.flatten(1) if v_new.dim() == 3 else v_new
+    if k2.dim() != 2 or k2.stride(1) != 1 or v2.stride(1) != 1 or k2.stride(0) != v2.stride(0):
+        raise ValueError("k_new and v_new rows must have unit element stride and equal row "
+                         "strides")
+    if int(k2.shape[0]) != B or slot_mapping.numel() != B:
+        raise ValueError("k_new, v_new and slot_mapping must have one row per sequence")
+    rc = library().pa_decode_store(
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _dev(k2, "k_new", torch.bfloat16), _dev(v2, "v_new", torch.bfloat16), int(k2.stride(0)),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(slot_mapping, "slot_mapping", torch.int32),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), B, num_blocks, hq, hkv, dq, bs,
+        int(max_context_len), float(scale), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream))
+    _check("pa_decode_store", rc)
 
 
 def pa_prefill_varlen(out, q, k_cache, v_cache, cu_seqlens_q, context_lens, block_table,

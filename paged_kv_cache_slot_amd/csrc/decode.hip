@@ -100,10 +100,19 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
     const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ context_lens, int32_t batch, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t log2_bs, int32_t max_context_len, float scale_log2,
-    char* __restrict__ ws, int32_t zero) {
+    char* __restrict__ ws, int32_t zero, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int64_t kv_stride,
+    const int32_t* __restrict__ slot_mapping, uint16_t* k_store, uint16_t* v_store) {
   // `zero` is always 0. Adding it to the address of a stand-in load keeps the
   // compiler from merging that load with an identical one (and from turning
   // the stand-in back into a branch).
+  //
+  // Fused store (slot_mapping != nullptr): row b's new token, at position
+  // L - 1, has its K/V in k_new/v_new row b and belongs in pool slot
+  // slot_mapping[b] (-1: already stored). The wavefront holding a pair's last
+  // chunk reads that token from k_new/v_new instead of the pool and writes it
+  // into the pool (k_store/v_store, the same pools); nothing else in the
+  // kernel reads that slot.
   constexpr int W = decode_waves<G>();
   constexpr int kThreads = 64 * W;
   constexpr int T = 4 * CH;  // tokens per chunk
@@ -296,6 +305,12 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
       qv[hh][0] = t.x; qv[hh][1] = t.y; qv[hh][2] = t.z; qv[hh][3] = t.w;
     }
   };
+  // The pool slot the segment's new token goes to: only a segment that ends
+  // its pair's context, with a fused store; else -1.
+  auto load_ns = [&](const Seg& it) -> int {
+    if (slot_mapping == nullptr || !it.valid || it.L <= 0 || it.tend != it.L) return -1;
+    return slot_mapping[it.b];
+  };
 
   // ---- one chunk: loads, then arithmetic ------------------------------------
   // Chunk c of a segment covers tokens t0 + T*c .. t0 + T*c + T - 1; row grp of
@@ -303,9 +318,13 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   // re-read the chunk's first token (cached), tokens past it inside the last
   // group re-read token tend-1 of the same block, and a chunk with no tokens at
   // all reads the segment's q row.
-  auto issue = [&](const Seg& it, int my_blk, int c, uint4 (&kb)[CH], uint4 (&vb)[CH]) {
+  auto issue = [&](const Seg& it, int my_blk, int ns, int c, uint4 (&kb)[CH],
+                   uint4 (&vb)[CH]) {
     const int cbase = it.t0 + c * T;
     const bool active = cbase < it.tend;  // uniform
+    // The new token's row comes from k_new/v_new when this chunk holds it.
+    const int new_tok = ns >= 0 && cbase + T > it.L - 1 ? it.L - 1 : -1;
+    const int64_t new_off = static_cast<int64_t>(it.b) * kv_stride + it.g * kHeadDim + sub * 8;
     const int bidx0 = it.t0 >> log2_bs;
     const int ngroups = min(CH, (it.tend - cbase + 3) >> 2);
     const int64_t head_off = it.g * kHeadDim + sub * 8;
@@ -324,8 +343,9 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
       const int64_t o =
           ((static_cast<int64_t>(blk) << log2_bs) | (tc & bs_mask)) * slot_stride + head_off;
       const int64_t off = j < ngroups ? o : off0;
-      kp[j] = active ? k_cache + off : dummy;
-      vp[j] = active ? v_cache + off : dummy;
+      const bool fresh = active && tc == new_tok;
+      kp[j] = fresh ? k_new + new_off : (active ? k_cache + off : dummy);
+      vp[j] = fresh ? v_new + new_off : (active ? v_cache + off : dummy);
     }
 #pragma unroll
     for (int j = 0; j < CH; ++j) kb[j] = load_stream(kp[j]);
@@ -345,10 +365,20 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
       for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
     }
   };
-  auto compute = [&](const Seg& it, int c, const uint32_t (&qv)[G][4], const uint4 (&kb)[CH],
-                     const uint4 (&vb)[CH]) {
+  auto compute = [&](const Seg& it, int ns, int c, const uint32_t (&qv)[G][4],
+                     const uint4 (&kb)[CH], const uint4 (&vb)[CH]) {
     const int cbase = it.t0 + c * T;
     if (cbase >= it.tend) return;  // uniform
+    if (ns >= 0 && cbase + T > it.L - 1) {  // this chunk holds the new token: store it
+      const int64_t dst = static_cast<int64_t>(ns) * slot_stride + it.g * kHeadDim + sub * 8;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        if (cbase + 4 * j + grp == it.L - 1) {
+          store_stream(k_store + dst, kb[j]);
+          store_stream(v_store + dst, vb[j]);
+        }
+      }
+    }
     float s[CH][G];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
@@ -453,28 +483,31 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   Seg ia = next_seg(Seg{0, wb, wg, 0, 0, 0, 0, 0, 0, 0});
   if (ia.valid) {
   int blk_a = load_blocks(ia);
+  int ns_a = load_ns(ia);
   uint32_t q_a[G][4], q_b[G][4];
   load_q(ia, q_a);
   uint4 kr0[CH], vr0[CH], kr1[CH], vr1[CH];
-  issue(ia, blk_a, 0, kr0, vr0);
+  issue(ia, blk_a, ns_a, 0, kr0, vr0);
   Seg ib = next_seg(ia);
   int blk_b = load_blocks(ib);
+  int ns_b = load_ns(ib);
   load_q(ib, q_b);
 
   // Processes `cur` (its first chunk in flight in buffer 0), requests `nxt`'s
   // first chunk, then refills cur's slot with the segment after `nxt`. Returns
   // false when `nxt` does not exist.
-  auto run = [&](Seg& cur, int& cur_blk, uint32_t (&qc)[G][4], const Seg& nxt, int nxt_blk)
-      -> bool {
+  auto run = [&](Seg& cur, int& cur_blk, int& cur_ns, uint32_t (&qc)[G][4], const Seg& nxt,
+                 int nxt_blk, int nxt_ns) -> bool {
     if (cur.first) reset();
     const int nch = max(0, (cur.tend - cur.t0 + T - 1) / T);
     for (int c = 0;; c += 2) {
-      issue(cur, cur_blk, c + 1, kr1, vr1);
-      compute(cur, c, qc, kr0, vr0);
+      issue(cur, cur_blk, cur_ns, c + 1, kr1, vr1);
+      compute(cur, cur_ns, c, qc, kr0, vr0);
       // Next: chunk c+2 of this segment, or the next segment's first chunk.
       const bool last = c + 2 >= nch;
-      issue(last ? nxt : cur, last ? nxt_blk : cur_blk, last ? 0 : c + 2, kr0, vr0);
-      compute(cur, c + 1, qc, kr1, vr1);
+      issue(last ? nxt : cur, last ? nxt_blk : cur_blk, last ? nxt_ns : cur_ns,
+            last ? 0 : c + 2, kr0, vr0);
+      compute(cur, cur_ns, c + 1, qc, kr1, vr1);
       // Wavefronts sharing a SIMD do not progress at the same rate, and every
       // range holds the same work: one behind its work-group's mean progress
       // issues at a higher priority.
@@ -491,12 +524,13 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
     if (!nxt.valid) return false;
     cur = next_seg(nxt);
     cur_blk = load_blocks(cur);
+    cur_ns = load_ns(cur);
     load_q(cur, qc);
     return true;
   };
   for (;;) {
-    if (!run(ia, blk_a, q_a, ib, blk_b)) break;
-    if (!run(ib, blk_b, q_b, ia, blk_a)) break;
+    if (!run(ia, blk_a, ns_a, q_a, ib, blk_b, ns_b)) break;
+    if (!run(ib, blk_b, ns_b, q_b, ia, blk_a, ns_a)) break;
   }
   }
 }
@@ -604,7 +638,7 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                  const uint16_t* v_cache, const int32_t* block_table, int32_t bt_stride,
                  const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                  int32_t num_kv_heads, int32_t log2_bs, int32_t max_context_len, float scale_log2,
-                 char* workspace, hipStream_t stream, hipError_t* err) {
+                 char* workspace, const FusedStore& fs, hipStream_t stream, hipError_t* err) {
   constexpr int W = decode_waves<G>();
   const int nb = std::min(batch, kScanRows);
   // No more work-groups than the most work these rows can hold needs (the
@@ -619,7 +653,8 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
   hipLaunchKernelGGL((decode_kernel<G, CH>), dim3(static_cast<uint32_t>(groups)), dim3(64 * W),
                      0, stream, out, q, k_cache, v_cache, block_table, bt_stride, context_lens,
                      nb, num_q_heads, num_kv_heads, log2_bs, max_context_len, scale_log2,
-                     workspace, 0);
+                     workspace, 0, fs.k_new, fs.v_new, fs.kv_stride, fs.slot_mapping,
+                     fs.k_store, fs.v_store);
   *err = hipGetLastError();
   if (*err == hipSuccess) {
     const int merge_groups = (groups * W + kMergeWaves - 1) / kMergeWaves;
@@ -662,7 +697,7 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          int32_t block_table_stride, const int32_t* context_lens, int32_t batch,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t block_size,
                          int32_t max_context_len, float scale, void* workspace,
-                         hipStream_t stream) {
+                         const FusedStore& fused, hipStream_t stream) {
   const int log2_bs = __builtin_ctz(static_cast<unsigned>(block_size));
   const float scale_log2 = scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
@@ -671,6 +706,12 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   // using the workspace from its start (the previous slice is merged by then).
   for (int b0 = 0; b0 < batch && err == hipSuccess;) {
     const int64_t row = static_cast<int64_t>(b0) * num_q_heads * kHeadDim;
+    FusedStore fs = fused;
+    if (fs.slot_mapping) {
+      fs.k_new += b0 * fs.kv_stride;
+      fs.v_new += b0 * fs.kv_stride;
+      fs.slot_mapping += b0;
+    }
     int done = 0;
 #define PA_DECODE_CASE(GG, CC)                                                              \
   case GG:                                                                                 \
@@ -678,7 +719,8 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                                 block_table + static_cast<int64_t>(b0) * block_table_stride, \
                                 block_table_stride, context_lens + b0, batch - b0,         \
                                 num_q_heads, num_kv_heads, log2_bs, max_context_len,       \
-                                scale_log2, static_cast<char*>(workspace), stream, &err);  \
+                                scale_log2, static_cast<char*>(workspace), fs, stream,     \
+                                &err);                                                     \
     break;
   switch (G) {
     PA_DECODE_CASE(1, 4)

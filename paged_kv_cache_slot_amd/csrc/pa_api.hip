@@ -114,7 +114,45 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
       static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table,
       block_table_stride, context_lens, batch, num_q_heads, num_kv_heads, block_size,
-      max_context_len, scale, workspace, static_cast<hipStream_t>(stream)));
+      max_context_len, scale, workspace, pa::FusedStore{}, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode_store(void* out, const void* q, const void* k_new, const void* v_new,
+                    int64_t kv_token_stride, void* k_cache, void* v_cache,
+                    const int32_t* slot_mapping, const int32_t* block_table,
+                    int32_t block_table_stride, const int32_t* context_lens, int32_t batch,
+                    int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_context_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || num_blocks < 0 || max_context_len < 0 || block_table_stride < 0 ||
+      !valid_scale(scale))
+    return PA_ERR_SHAPE;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (static_cast<int64_t>(block_table_stride) * block_size < max_context_len)
+    return PA_ERR_SHAPE;
+  if (kv_token_stride < static_cast<int64_t>(num_kv_heads) * head_dim) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !slot_mapping || !block_table ||
+      !context_lens)
+    return PA_ERR_NULL;
+  if (kv_token_stride % 8 != 0 || !aligned16(out) || !aligned16(q) || !aligned16(k_new) ||
+      !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const size_t need = pa::decode_workspace_bytes(batch, num_q_heads, max_context_len);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+  pa::FusedStore fs;
+  fs.k_new = static_cast<const uint16_t*>(k_new);
+  fs.v_new = static_cast<const uint16_t*>(v_new);
+  fs.kv_stride = kv_token_stride;
+  fs.slot_mapping = slot_mapping;
+  fs.k_store = static_cast<uint16_t*>(k_cache);
+  fs.v_store = static_cast<uint16_t*>(v_cache);
+  return from_hip(pa::launch_decode(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table,
+      block_table_stride, context_lens, batch, num_q_heads, num_kv_heads, block_size,
+      max_context_len, scale, workspace, fs, static_cast<hipStream_t>(stream)));
 }
 
 int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -273,18 +311,21 @@ int check_step_buffers(const pa_decode_step_buffers& b, int32_t batch) {
   return PA_OK;
 }
 
-// Records the decode step for `batch` rows on `stream` (which is capturing).
+// Records the decode step for `batch` rows on `stream` (which is capturing):
+// the store fused into the decode launch, as pa_decode_store runs it.
 hipError_t record_step(const pa_decode_step_buffers& b, int32_t batch, hipStream_t stream) {
-  hipError_t e = pa::launch_store_kvcache(
-      static_cast<const uint16_t*>(b.k_new), static_cast<const uint16_t*>(b.v_new),
-      b.kv_token_stride, static_cast<uint16_t*>(b.k_cache), static_cast<uint16_t*>(b.v_cache),
-      b.slot_mapping, batch, b.num_kv_heads, stream);
-  if (e != hipSuccess) return e;
+  pa::FusedStore fs;
+  fs.k_new = static_cast<const uint16_t*>(b.k_new);
+  fs.v_new = static_cast<const uint16_t*>(b.v_new);
+  fs.kv_stride = b.kv_token_stride;
+  fs.slot_mapping = b.slot_mapping;
+  fs.k_store = static_cast<uint16_t*>(b.k_cache);
+  fs.v_store = static_cast<uint16_t*>(b.v_cache);
   return pa::launch_decode(
       static_cast<uint16_t*>(b.out), static_cast<const uint16_t*>(b.q),
       static_cast<const uint16_t*>(b.k_cache), static_cast<const uint16_t*>(b.v_cache),
       b.block_table, b.block_table_stride, b.context_lens, batch, b.num_q_heads,
-      b.num_kv_heads, b.block_size, b.max_context_len, b.scale, b.workspace, stream);
+      b.num_kv_heads, b.block_size, b.max_context_len, b.scale, b.workspace, fs, stream);
 }
 
 }  // namespace

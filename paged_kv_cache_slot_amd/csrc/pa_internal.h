@@ -23,12 +23,26 @@ hipError_t launch_store_kvcache(const uint16_t* k, const uint16_t* v, int64_t kv
                                 const int32_t* slot_mapping, int32_t num_tokens,
                                 int32_t num_kv_heads, hipStream_t stream);
 
+// A store fused into a decode launch: row b's new token (position
+// context_lens[b] - 1) has its K/V in row b of k_new/v_new (token stride
+// kv_stride elements) and goes into pool slot slot_mapping[b] (-1: already in
+// the pool). k_store/v_store are the pools decode reads. No fused store when
+// slot_mapping is null.
+struct FusedStore {
+  const uint16_t* k_new = nullptr;
+  const uint16_t* v_new = nullptr;
+  int64_t kv_stride = 0;
+  const int32_t* slot_mapping = nullptr;
+  uint16_t* k_store = nullptr;
+  uint16_t* v_store = nullptr;
+};
+
 hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                          const uint16_t* v_cache, const int32_t* block_table,
                          int32_t block_table_stride, const int32_t* context_lens, int32_t batch,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t block_size,
                          int32_t max_context_len, float scale, void* workspace,
-                         hipStream_t stream);
+                         const FusedStore& fused, hipStream_t stream);
 
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_context_len);
 

@@ -95,6 +95,35 @@ def test_decode_argument_checks(lib):
         assert call(scale=bad) == PA_ERR_SHAPE
 
 
+def test_decode_store_argument_checks(lib):
+    f = lib.pa_decode_store
+    P = _fake()
+    ws = pa.pa_decode_workspace_bytes(4, 16, 128, 300, 256)
+    base = dict(out=P, q=P, kn=P, vn=P, kvs=1024, kc=P, vc=P, sm=P, bt=P, stride=2, cl=P, B=4,
+                nb=10, hq=16, hkv=8, d=128, bs=256, maxl=300, scale=0.088, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["out"], a["q"], a["kn"], a["vn"], a["kvs"], a["kc"], a["vc"], a["sm"], a["bt"],
+                 a["stride"], a["cl"], a["B"], a["nb"], a["hq"], a["hkv"], a["d"], a["bs"],
+                 a["maxl"], a["scale"], a["ws"], a["wsb"], None)
+
+    assert call(B=0) == PA_OK
+    for name in ("out", "q", "kn", "vn", "kc", "vc", "sm", "bt", "cl"):
+        assert call(**{name: None}) == PA_ERR_NULL, name
+    assert call(kvs=1000) == PA_ERR_SHAPE          # stride < Hkv * D
+    assert call(kvs=1028) == PA_ERR_UNSUPPORTED    # stride % 8
+    assert call(kn=_fake(0x10002)) == PA_ERR_UNSUPPORTED
+    assert call(nb=-1) == PA_ERR_SHAPE
+    assert call(hq=24, hkv=8) == PA_ERR_UNSUPPORTED  # G = 3
+    assert call(d=64) == PA_ERR_UNSUPPORTED
+    assert call(stride=1) == PA_ERR_SHAPE          # 1 block cannot hold 300 tokens
+    assert call(wsb=ws - 1) == PA_ERR_WORKSPACE
+    assert call(ws=None) == PA_ERR_WORKSPACE
+    for bad in (0.0, -0.088, float("nan"), float("inf")):
+        assert call(scale=bad) == PA_ERR_SHAPE
+
+
 def test_prefill_argument_checks(lib):
     f = lib.pa_prefill_varlen
     P = _fake()

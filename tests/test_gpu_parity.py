@@ -184,6 +184,78 @@ def test_decode_long_rows_many_pieces(bs, hq, hkv, lens):
             assert int(out[b].float().abs().sum()) == 0
 
 
+FUSED_CASES = [
+    # (block_size, Hq, Hkv, lengths): ragged tails, padding rows, pairs cut many times
+    (16, 32, 8, [1, 15, 16, 17, 255, 256, 257, 600, 1023, 0, 2048, 333]),
+    (256, 16, 8, [1, 255, 256, 257, 0, 1100, 77, 40000]),
+    (64, 8, 8, [12345, 2, 0, 64]),
+    (128, 64, 8, [100, 1500, 0, 1]),
+]
+
+
+def _fused_vs_separate(case, say_what):
+    """Runs the decode step twice on copies of the pools: pa_store_kvcache then
+    pa_decode, and pa_decode_store. Returns (separate out, fused out, pools...)."""
+    kc0, vc0 = case["k_cache"].clone(), case["v_cache"].clone()
+    gpu_store(case)
+    sep = gpu_decode(case)
+    kc_sep, vc_sep = case["k_cache"].clone(), case["v_cache"].clone()
+    case["k_cache"].copy_(kc0)
+    case["v_cache"].copy_(vc0)
+    B, hq, d = case["q"].shape
+    out = torch.full_like(case["q"], float("nan"))
+    ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(B, hq, d, case["max_context_len"],
+                                                          case["block_size"])),
+                     dtype=torch.uint8, device=DEV)
+    say(f"[case] {say_what}")
+    pa.pa_decode_store(out, case["q"], case["k_new"], case["v_new"], case["k_cache"],
+                       case["v_cache"], case["slot_mapping"], case["block_table"],
+                       case["context_lens"], case["max_context_len"], case["scale"], ws)
+    torch.cuda.synchronize()
+    return sep, out, kc_sep, vc_sep
+
+
+@pytest.mark.parametrize("bs,hq,hkv,lens", FUSED_CASES,
+                         ids=[f"bs{a}-hq{b}-hkv{c}" for a, b, c, _ in FUSED_CASES])
+def test_decode_store_fused_equals_separate(bs, hq, hkv, lens):
+    """pa_decode_store gives the output and pools of pa_store_kvcache + pa_decode,
+    bit for bit, and the output matches the oracle."""
+    case = workloads.decode_case(len(lens), (1, 2048), hq, hkv, 128, bs, seed=900 + bs + hq,
+                                 device=DEV, lens=lens, spare_blocks=3)
+    h = host_copy(case)
+    sep, fused, kc_sep, vc_sep = _fused_vs_separate(
+        case, f"fused decode store bs={bs} Hq={hq} Hkv={hkv} lens={lens}")
+    assert torch.equal(case["k_cache"], kc_sep) and torch.equal(case["v_cache"], vc_sep)
+    assert torch.equal(fused, sep)
+    kc, vc = oracle_after_store(h)
+    ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
+                        nthreads=ORACLE_THREADS)
+    compare(fused, ref, "fused decode store")
+
+
+def test_decode_store_fused_large_batch_and_prestored_rows():
+    """More rows than one launch covers (the fused store follows each slice), and
+    live rows whose new token is already in the pool (slot -1): every row and
+    both pools equal the separate calls."""
+    rng = np.random.default_rng(8)
+    lens = rng.integers(1, 600, size=1500)
+    lens[rng.choice(1500, size=60, replace=False)] = 0
+    case = workloads.decode_case(1500, (1, 600), 16, 8, 128, 16, seed=8, device=DEV, lens=lens)
+    # Rows 0..99 have their new token stored up front and pass slot -1.
+    pre = torch.arange(100, device=DEV)
+    live = case["slot_mapping"][pre] >= 0
+    pa.pa_store_kvcache(case["k_new"][pre], case["v_new"][pre], case["k_cache"], case["v_cache"],
+                        case["slot_mapping"][pre].contiguous())
+    slots = case["slot_mapping"].clone()
+    slots[pre] = -1
+    case = dict(case, slot_mapping=slots)
+    torch.cuda.synchronize()
+    assert int(live.sum()) > 90
+    sep, fused, kc_sep, vc_sep = _fused_vs_separate(case, "fused decode store, 1500 rows")
+    assert torch.equal(case["k_cache"], kc_sep) and torch.equal(case["v_cache"], vc_sep)
+    assert torch.equal(fused, sep)
+
+
 def test_decode_more_rows_than_one_scan_window():
     """2600 rows (more than the 1024 rows of context lengths a work-group holds in
     LDS at once), mixed lengths and padding: every row against the oracle."""
