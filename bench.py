@@ -102,21 +102,32 @@ def prefill_flops(case):
 
 # ----------------------------------------------------------------- timing --
 
+class _no_gc:
+    """Pauses Python's garbage collector (without running it) inside a timed
+    region: a full collection can stall the launching thread for tens of
+    milliseconds, and the GPU idle it causes lowers its clocks (measured: a
+    50 ms idle gap before a warm-up slows the next Qwen3-8B decode steps by
+    about 10%)."""
+
+    def __enter__(self):
+        import gc
+        self.was_enabled = gc.isenabled()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        import gc
+        if self.was_enabled:
+            gc.enable()
+
+
 def run_timed(step, warmup, steps):
     """Warm up, then time exactly `steps` calls of step(i) between two device
-    synchronisations. Returns (ms per step, [per-step kernel ms]). Python's
-    garbage collector is paused (not run) from the warm-up to the end of the
-    timed steps: a full collection can stall the launching thread for tens of
-    milliseconds, and the GPU idle it causes lowers its clocks (measured: a
-    50 ms idle gap before the warm-up slows the next Qwen3-8B decode steps by
-    about 10%)."""
-    import gc
+    synchronisations, with the garbage collector paused (see _no_gc). Returns
+    (ms per step, [per-step kernel ms])."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    was_enabled = gc.isenabled()
-    gc.disable()
-    try:
+    with _no_gc():
         for i in range(warmup):
             step(i, None)
         torch.cuda.synchronize()
@@ -125,9 +136,6 @@ def run_timed(step, warmup, steps):
             step(i, evs[i])
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
-    finally:
-        if was_enabled:
-            gc.enable()
     return ms, [a.elapsed_time(b) for a, b in evs]
 
 
@@ -336,22 +344,23 @@ def graph_bench(batches=(1, 4, 16, 64, 256), steps=200, warmup=10):
 
         row = {"batch": batch, "bucket": bucket}
         for name, fn in (("eager", eager), ("graph", graph)):
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
-            # Dependent steps: the host waits for each step before the next, as
-            # a serving loop must (the next step's tokens come from this one).
-            t0 = time.perf_counter()
-            for _ in range(steps):
-                fn()
+            with _no_gc():
+                for _ in range(warmup):
+                    fn()
                 torch.cuda.synchronize()
-            row[f"{name}_dependent_us"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
-            # Pipelined steps: enqueued back to back, one wait at the end.
-            t0 = time.perf_counter()
-            for _ in range(steps):
-                fn()
-            torch.cuda.synchronize()
-            row[f"{name}_pipelined_us"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+                # Dependent steps: the host waits for each step before the next, as
+                # a serving loop must (the next step's tokens come from this one).
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    fn()
+                    torch.cuda.synchronize()
+                row[f"{name}_dependent_us"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+                # Pipelined steps: enqueued back to back, one wait at the end.
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    fn()
+                torch.cuda.synchronize()
+                row[f"{name}_pipelined_us"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
         row["dependent_speedup"] = round(row["eager_dependent_us"] / row["graph_dependent_us"], 3)
         row["pipelined_speedup"] = round(row["eager_pipelined_us"] / row["graph_pipelined_us"], 3)
         res.append(row)
@@ -377,16 +386,17 @@ def sampler_bench(warmup, steps, B=256, V=151936):
     tok = torch.empty(B, dtype=torch.int32, device="cuda")
     ws = torch.empty(pa.pa_sample_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        pa.pa_sample_gumbel(tok, probs, 1, i, ws)
-    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        pa.pa_sample_gumbel(tok, probs, 1, warmup + i, ws)
-        b.record(stream)
-    torch.cuda.synchronize()
+    with _no_gc():
+        for i in range(warmup):
+            pa.pa_sample_gumbel(tok, probs, 1, i, ws)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            pa.pa_sample_gumbel(tok, probs, 1, warmup + i, ws)
+            b.record(stream)
+        torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     nbytes = B * V * 4 + B * 4
     sample_rows = 8
