@@ -102,6 +102,14 @@ def prefill_flops(case):
 
 # ----------------------------------------------------------------- timing --
 
+# Warm-up of the secondary legs: at least this many steps and this many
+# seconds of them. Measured in a fresh process, the Qwen3-8B decode steps get
+# faster over the first seconds of GPU work (389 -> 363 us over four 20-step
+# runs), so a few warm-up steps leave those legs below their steady state.
+SECONDARY_WARMUP = 10
+SECONDARY_WARM_S = 0.5
+
+
 class _no_gc:
     """Pauses Python's garbage collector (without running it) inside a timed
     region: a full collection can stall the launching thread for tens of
@@ -120,7 +128,7 @@ class _no_gc:
             gc.enable()
 
 
-def run_timed(step, warmup, steps):
+def run_timed(step, warmup, steps, warm_s=0.0):
     """Warm up, then time exactly `steps` calls of step(i) between two device
     synchronisations, with the garbage collector paused (see _no_gc). Returns
     (ms per step, [per-step kernel ms])."""
@@ -128,8 +136,13 @@ def run_timed(step, warmup, steps):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     with _no_gc():
-        for i in range(warmup):
+        t_w = time.perf_counter()
+        i = 0
+        while i < warmup or time.perf_counter() - t_w < warm_s:
             step(i, None)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
@@ -139,7 +152,7 @@ def run_timed(step, warmup, steps):
     return ms, [a.elapsed_time(b) for a, b in evs]
 
 
-def decode_bench(name, warmup, steps, fused=True):
+def decode_bench(name, warmup, steps, fused=True, warm_s=0.0):
     import torch
     import numpy as np
     import paged_kv_cache_slot_amd as pa
@@ -171,7 +184,7 @@ def decode_bench(name, warmup, steps, fused=True):
         if ev:
             ev[1].record()
 
-    ms, kms = run_timed(step, warmup, steps)
+    ms, kms = run_timed(step, warmup, steps, warm_s)
     # The same call again with the 256 MB last-level cache (MALL) overwritten
     # before each one (a 512 MiB fill outside the timed events), so that no
     # part of the pool can be served from it: median of the decode calls.
@@ -198,7 +211,7 @@ def decode_bench(name, warmup, steps, fused=True):
     return res
 
 
-def prefill_bench(warmup, steps):
+def prefill_bench(warmup, steps, warm_s=0.0):
     import torch
     import numpy as np
     import paged_kv_cache_slot_amd as pa
@@ -218,7 +231,7 @@ def prefill_bench(warmup, steps):
         if ev:
             ev[1].record()
 
-    ms, kms = run_timed(step, warmup, steps)
+    ms, kms = run_timed(step, warmup, steps, warm_s)
     flops = prefill_flops(case)
     kern_ms = float(np.mean(kms))
     return dict(ms_per_step=ms, flops=flops, prefill_ms=kern_ms,
@@ -471,7 +484,8 @@ def main():
         log("[bench] copied 1 GiB 5 times")
         return
     if args.profile_leg:
-        fn = {"prefill": lambda: prefill_bench(args.warmup, args.steps),
+        fn = {"prefill": lambda: prefill_bench(max(args.warmup, SECONDARY_WARMUP), args.steps,
+                                               warm_s=SECONDARY_WARM_S),
               "sampler": lambda: sampler_bench(args.warmup, args.steps)}[args.profile_leg]
         res = fn()
         print(json.dumps({k: v for k, v in res.items() if k != "case"}), flush=True)
@@ -499,7 +513,8 @@ def main():
     if not args.no_secondary:
         for name in ("qwen3_8b_decode", "bs16_stress_decode"):
             log(f"[bench] {name}: decode step (store fused into decode)")
-            r = decode_bench(name, args.warmup, args.steps)
+            r = decode_bench(name, max(args.warmup, SECONDARY_WARMUP), args.steps,
+                             warm_s=SECONDARY_WARM_S)
             secondary.append({
                 "workload": name, "ms_per_step": round(r["ms_per_step"], 4),
                 "step_GBps": round(r["gbs"], 2),
@@ -511,7 +526,8 @@ def main():
             del r
             torch.cuda.empty_cache()
         log("[bench] qwen3_8b_prefill_prefix: store + prefill")
-        r = prefill_bench(args.warmup, args.steps)
+        r = prefill_bench(max(args.warmup, SECONDARY_WARMUP), args.steps,
+                          warm_s=SECONDARY_WARM_S)
         secondary.append({
             "workload": "qwen3_8b_prefill_prefix",
             "ms_per_step": round(r["ms_per_step"], 4), "prefill_us": round(r["prefill_ms"] * 1e3, 2),
