@@ -49,10 +49,17 @@ def log(*a):
 
 
 def source_digest(*names):
+    """Digest of the code of the named sources: comments and whitespace are
+    removed first, so that only a change to the code itself invalidates the
+    counter record taken on it."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_slot_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_slot_amd", "csrc", n), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

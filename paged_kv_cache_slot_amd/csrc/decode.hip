@@ -34,8 +34,17 @@
 // per chunk; p*V accumulated in fp32. At the end of a pair the four rows of
 // lanes are merged with the usual (max, sum, acc) rescaling.
 //
+// Each wavefront also records, at its start, the merge job of the range
+// boundary at its first unit (which pair it cuts, which wavefronts hold the
+// pieces), so that the merge reads its job in one round of loads.
+//
+// With a fused store (the decode step's pa_store_kvcache folded in), the
+// wavefront holding a pair's last chunk reads the new token (position L - 1)
+// from the step's input rows and writes it into the pool slot it belongs in.
+//
 // Roofline: HBM. Algorithmic bytes = 2 (K and V) * L * 256 B per (sequence,
-// kv head), plus q and out, which are small.
+// kv head), plus q and out, which are small (plus the new tokens' rows written
+// into the pools when the store is fused).
 #include <algorithm>
 #include <atomic>
 #include <cmath>
