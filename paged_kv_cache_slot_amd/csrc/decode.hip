@@ -56,11 +56,25 @@ namespace {
 
 constexpr int kScanRows = 1024;        // sequences per launch (their lengths sit in LDS)
 constexpr int kPairCost = 2;           // per-(sequence, kv head) overhead, in chunk units
-constexpr int kMinUnits = 16;          // fewest cost units a wavefront is given
+constexpr int kMinUnits = 16;          // cost units per wavefront once kFillWaves are busy
+constexpr int kFewUnits = 4;           // fewest cost units a wavefront is given
+constexpr int64_t kFillWaves = 2048;   // working wavefronts that keep HBM streaming
 constexpr float kLazyLog2 = 8.f;       // headroom of the softmax reference (log2 units)
 constexpr int kRecord = 132;           // floats per partial record: acc[128], max, sum, pad
 constexpr int kInfoOffset = 64;        // workspace bytes before the per-wavefront records
 constexpr int kMergeWaves = 16;        // wavefronts per work-group of the merge
+
+// Working wavefronts for a cost line of C units, before the grid's cap. A
+// wavefront is given kMinUnits units; when that leaves fewer than kFillWaves
+// wavefronts, it is given fewer (down to kFewUnits): a small batch is bound by
+// the latency of each wavefront's chain of chunks, not by HBM, and the extra
+// pieces cost only their merge. Non-decreasing in C.
+__host__ __device__ inline int64_t wave_target(int64_t C) {
+  const int64_t few = C / kFewUnits;
+  const int64_t fill = few < kFillWaves ? few : kFillWaves;
+  const int64_t full = C / kMinUnits;
+  return full > fill ? full : fill;
+}
 
 // Workspace layout. Header (int64): the total cost C and the number of working
 // wavefronts nw. Then per wavefront w < nw, the merge job of the range
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   __syncthreads();  // the only work-group barriers: from here on wavefronts run independently
 
   const int64_t nw = std::max<int64_t>(
-      1, std::min<int64_t>(static_cast<int64_t>(gridDim.x) * W, C / kMinUnits));
+      1, std::min<int64_t>(static_cast<int64_t>(gridDim.x) * W, wave_target(C)));
   int64_t* hdr = reinterpret_cast<int64_t*>(ws);
   int64_t* info = reinterpret_cast<int64_t*>(ws + kInfoOffset);
   float* part = reinterpret_cast<float*>(ws + partial_offset(nw));
@@ -651,14 +665,13 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
   constexpr int W = decode_waves<G>();
   const int nb = std::min(batch, kScanRows);
   // No more work-groups than the most work these rows can hold needs (the
-  // kernel gives a wavefront at least kMinUnits units): small batches then do
+  // kernel's wave_target is non-decreasing in the cost): small batches then do
   // not start a work-group per CU only to scan context_lens and leave.
   const int64_t max_units =
       static_cast<int64_t>(nb) * num_kv_heads *
       ((std::max(0, max_context_len) + 4 * CH - 1) / (4 * CH) + kPairCost);
   const int groups = static_cast<int>(std::max<int64_t>(
-      1, std::min<int64_t>(resident_groups<G, CH>(),
-                           (max_units + kMinUnits * W - 1) / (kMinUnits * W))));
+      1, std::min<int64_t>(resident_groups<G, CH>(), (wave_target(max_units) + W - 1) / W)));
   hipLaunchKernelGGL((decode_kernel<G, CH>), dim3(static_cast<uint32_t>(groups)), dim3(64 * W),
                      0, stream, out, q, k_cache, v_cache, block_table, bt_stride, context_lens,
                      nb, num_q_heads, num_kv_heads, log2_bs, max_context_len, scale_log2,
@@ -688,16 +701,20 @@ void prepare_decode(int32_t num_q_heads, int32_t num_kv_heads) {
 }
 
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_context_len) {
-  // Per launch (at most kScanRows sequences): nw <= max(1, C / kMinUnits) working
-  // wavefronts, with C <= rows * Hkv * (ceil(max_context_len / 8) + kPairCost)
-  // (a chunk holds at least 8 tokens); and nw * G <= rows * Hq * (...) /
-  // kMinUnits + Hq, since G * Hkv = Hq and G <= Hq.
+  // Per launch (at most kScanRows sequences): nw <= max(1, wave_target(C))
+  // working wavefronts, with C <= rows * Hkv * (ceil(max_context_len / 8) +
+  // kPairCost) (a chunk holds at least 8 tokens). With U = rows * Hq * (...),
+  // G * Hkv = Hq and G <= Hq: nw <= max(U / kMinUnits, min(U / kFewUnits,
+  // kFillWaves)) + 1 and nw * G <= max(U / kMinUnits, min(U / kFewUnits,
+  // Hq * kFillWaves)) + Hq.
   if (batch <= 0) return 0;
   const int64_t rows = std::min(batch, kScanRows);
   const int64_t units = (std::max(0, max_context_len) + 7) / 8 + kPairCost;
-  const int64_t x = rows * num_q_heads * units / kMinUnits;
-  const int64_t nw = x + 1;                        // bound on nw (Hkv <= Hq)
-  const int64_t records = 2 * (x + num_q_heads);   // bound on 2 * nw * G
+  const int64_t u = rows * num_q_heads * units;
+  const int64_t nw = std::max(u / kMinUnits, std::min(u / kFewUnits, kFillWaves)) + 1;
+  const int64_t records =                          // bound on 2 * nw * G
+      2 * (std::max(u / kMinUnits, std::min(u / kFewUnits, num_q_heads * kFillWaves)) +
+           num_q_heads);
   return partial_offset(nw) + static_cast<size_t>(records) * kRecord * sizeof(float);
 }
 

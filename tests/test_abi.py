@@ -137,13 +137,17 @@ def test_prefill_argument_checks(lib):
 
 
 def test_workspace_size():
-    """Header (64 B) + per-wavefront record (4 int64) for nw <= x + 1 wavefronts
-    + 2 (x + Hq) partial records of 132 floats, x = rows * Hq * (ceil(L / 8) + 2)
-    // 16, rows = min(batch, 1024)."""
+    """Header (64 B) + per-wavefront record (4 int64) for nw <= t(2048) + 1
+    wavefronts + 2 (t(Hq * 2048) + Hq) partial records of 132 floats, where
+    t(f) = max(u // 16, min(u // 4, f)), u = rows * Hq * (ceil(L / 8) + 2),
+    rows = min(batch, 1024): a wavefront takes 16 cost units, or down to 4 while
+    fewer than 2048 wavefronts would work."""
     def expect(batch, hq, max_len):
         rows = min(batch, 1024)
-        x = rows * hq * ((max_len + 7) // 8 + 2) // 16
-        return 64 + (x + 1) * 32 + 2 * (x + hq) * 132 * 4
+        u = rows * hq * ((max_len + 7) // 8 + 2)
+        nw = max(u // 16, min(u // 4, 2048)) + 1
+        recs = max(u // 16, min(u // 4, hq * 2048)) + hq
+        return 64 + nw * 32 + 2 * recs * 132 * 4
     assert pa.pa_decode_workspace_bytes(256, 16, 128, 2048, 256) == 71877216 == expect(256, 16, 2048)
     for args in ((3, 4, 0), (3, 4, 257), (1, 32, 2048), (4096, 32, 2048)):
         assert pa.pa_decode_workspace_bytes(args[0], args[1], 128, args[2], 16) == expect(*args)
