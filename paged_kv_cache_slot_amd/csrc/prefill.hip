@@ -107,18 +107,14 @@ constexpr int kSchedDsRead = 0x100;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
 
-// 16 bytes per lane from global memory into LDS at dst + 16 * lane.
-__device__ __forceinline__ void dma16(const void* src, uint16_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(dst), 16, 0, 0);
-}
-
 // Raw buffer resource over [base, base + 2^31): scalar base, no stride, no
 // swizzle (dword 3 as for gfx9 raw buffers).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
 
-// Same as dma16 from a buffer: lane reads rsrc.base + soff + voff.
+// 16 bytes per lane from a buffer into LDS at dst + 16 * lane: lane reads
+// rsrc.base + soff + voff.
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff,
                                           uint16_t* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(dst), 16, voff, soff, 0, 0);
@@ -222,10 +218,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   // those and the 16-byte unit (l%16) of its LDS row, which holds logical unit
   // (l%16) ^ swz(key) of the key's 256-byte row.
   //
-  // Fast path (all 16 keys inside the context): the block's base address is
-  // scalar and each lane adds a fixed 32-bit offset (buffer_load ... lds).
-  // Keys past the context (only in a sequence's last tile) re-read token L-1
-  // instead, with per-lane addresses, so V never holds stale values there.
+  // All copies are buffer loads with a scalar base: the block holding key
+  // min(k0, L-1), k0 the first of the wavefront's 16 keys. Fast path (all 16
+  // keys inside the context): each lane adds a fixed 32-bit offset. Keys past
+  // the context (only in a sequence's last tile) re-read token L-1 instead, so
+  // V never holds stale values there; the group's keys that remain, and token
+  // L-1, then lie in that same block, so a per-lane offset from the same base
+  // still reaches them. (With the flat-encoded global form of these copies in
+  // flight the compiler no longer counts the LDS reads' waits exactly and
+  // waits for all of them; with buffer loads it does count them.)
   const int dma_row = lane >> 4;
   const int dma_unit = lane & 15;
   uint32_t lane_off[4];
@@ -234,17 +235,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     lane_off[j] = dma_row * slot_bytes + ((dma_unit ^ swz(4 * j + dma_row)) * 16);
   const char* kbase = reinterpret_cast<const char*>(k_cache) + g * (kHeadDim * 2);
   const char* vbase = reinterpret_cast<const char*>(v_cache) + g * (kHeadDim * 2);
-  // Block id of this wavefront's keys in tile t (any valid block past the end).
+  // Block id of key min(first of this wavefront's keys in tile t, L-1).
   auto block_of = [&](int t) { return bt[min(t * kKeys + 16 * wave, L - 1) >> log2_bs]; };
   auto issue_tile = [&](int t, int blk, uint16_t* lk, uint16_t* lv) {
     const int k0 = t * kKeys + 16 * wave;  // first key of this wavefront's 16
+    const int kfirst = min(k0, L - 1);
     uint16_t* dk = lk + 16 * wave * kHeadDim;
     uint16_t* dv = lv + 16 * wave * kHeadDim;
+    const int64_t first =
+        ((static_cast<int64_t>(blk) << log2_bs) | (kfirst & bs_mask)) * slot_bytes;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + first);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + first);
     if (k0 + 15 < L) {
-      const int64_t first =
-          ((static_cast<int64_t>(blk) << log2_bs) | (k0 & bs_mask)) * slot_bytes;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + first);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + first);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         dma16_buf(rk, lane_off[j], j * 4 * slot_bytes, dk + j * 4 * kHeadDim);
@@ -254,11 +256,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kc = min(k0 + 4 * j + dma_row, L - 1);
-        const int64_t slot =
-            (static_cast<int64_t>(bt[kc >> log2_bs]) << log2_bs) | (kc & bs_mask);
-        const int64_t off = slot * slot_bytes + ((dma_unit ^ swz(4 * j + dma_row)) * 16);
-        dma16(kbase + off, dk + j * 4 * kHeadDim);
-        dma16(vbase + off, dv + j * 4 * kHeadDim);
+        const uint32_t off = (kc - kfirst) * slot_bytes + ((dma_unit ^ swz(4 * j + dma_row)) * 16);
+        dma16_buf(rk, off, 0, dk + j * 4 * kHeadDim);
+        dma16_buf(rv, off, 0, dv + j * 4 * kHeadDim);
       }
     }
   };
