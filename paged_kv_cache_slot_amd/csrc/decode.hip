@@ -56,7 +56,7 @@ namespace {
 
 constexpr int kScanRows = 1024;        // sequences per launch (their lengths sit in LDS)
 constexpr int kPairCost = 2;           // per-(sequence, kv head) overhead, in chunk units
-constexpr int kMinUnits = 16;          // cost units per wavefront once kFillWaves are busy
+constexpr int kFullUnits = 16;         // cost units per wavefront once kFillWaves are busy
 constexpr int kFewUnits = 4;           // fewest cost units a wavefront is given
 constexpr int64_t kFillWaves = 2048;   // working wavefronts that keep HBM streaming
 constexpr float kLazyLog2 = 8.f;       // headroom of the softmax reference (log2 units)
@@ -65,14 +65,14 @@ constexpr int kInfoOffset = 64;        // workspace bytes before the per-wavefro
 constexpr int kMergeWaves = 16;        // wavefronts per work-group of the merge
 
 // Working wavefronts for a cost line of C units, before the grid's cap. A
-// wavefront is given kMinUnits units; when that leaves fewer than kFillWaves
+// wavefront is given kFullUnits units; when that leaves fewer than kFillWaves
 // wavefronts, it is given fewer (down to kFewUnits): a small batch is bound by
 // the latency of each wavefront's chain of chunks, not by HBM, and the extra
 // pieces cost only their merge. Non-decreasing in C.
 __host__ __device__ inline int64_t wave_target(int64_t C) {
   const int64_t few = C / kFewUnits;
   const int64_t fill = few < kFillWaves ? few : kFillWaves;
-  const int64_t full = C / kMinUnits;
+  const int64_t full = C / kFullUnits;
   return full > fill ? full : fill;
 }
 
@@ -704,16 +704,16 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_co
   // Per launch (at most kScanRows sequences): nw <= max(1, wave_target(C))
   // working wavefronts, with C <= rows * Hkv * (ceil(max_context_len / 8) +
   // kPairCost) (a chunk holds at least 8 tokens). With U = rows * Hq * (...),
-  // G * Hkv = Hq and G <= Hq: nw <= max(U / kMinUnits, min(U / kFewUnits,
-  // kFillWaves)) + 1 and nw * G <= max(U / kMinUnits, min(U / kFewUnits,
+  // G * Hkv = Hq and G <= Hq: nw <= max(U / kFullUnits, min(U / kFewUnits,
+  // kFillWaves)) + 1 and nw * G <= max(U / kFullUnits, min(U / kFewUnits,
   // Hq * kFillWaves)) + Hq.
   if (batch <= 0) return 0;
   const int64_t rows = std::min(batch, kScanRows);
   const int64_t units = (std::max(0, max_context_len) + 7) / 8 + kPairCost;
   const int64_t u = rows * num_q_heads * units;
-  const int64_t nw = std::max(u / kMinUnits, std::min(u / kFewUnits, kFillWaves)) + 1;
+  const int64_t nw = std::max(u / kFullUnits, std::min(u / kFewUnits, kFillWaves)) + 1;
   const int64_t records =                          // bound on 2 * nw * G
-      2 * (std::max(u / kMinUnits, std::min(u / kFewUnits, num_q_heads * kFillWaves)) +
+      2 * (std::max(u / kFullUnits, std::min(u / kFewUnits, num_q_heads * kFillWaves)) +
            num_q_heads);
   return partial_offset(nw) + static_cast<size_t>(records) * kRecord * sizeof(float);
 }
