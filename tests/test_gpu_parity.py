@@ -184,6 +184,31 @@ def test_decode_long_rows_many_pieces(bs, hq, hkv, lens):
             assert int(out[b].float().abs().sum()) == 0
 
 
+# Batches on both sides of the two points where the decode's wavefront count
+# changes regime. With 16 q / 8 kv heads, contexts U[900, 1100] and chunks of
+# 16 tokens, a (sequence, kv head) pair costs about 64.5 units, so the cost
+# line holds C ~ 516 B units: near B = 16, C / 4 reaches 2048 (below it every
+# wavefront takes 4 units); near B = 64, C / 16 does (above it 16 units each).
+CROSSOVER_BATCHES = [15, 16, 17, 62, 63, 64, 65]
+
+
+@pytest.mark.parametrize("batch", CROSSOVER_BATCHES)
+def test_decode_wave_count_crossovers(batch):
+    """Decode parity at batch sizes around both changes of the work share per
+    wavefront (4 units, then 2048 wavefronts, then 16 units)."""
+    say(f"[case] decode crossover batch={batch}")
+    case = workloads.decode_case(batch, (900, 1100), 16, 8, 128, 256, seed=700 + batch,
+                                 device=DEV)
+    h = host_copy(case)
+    gpu_store(case)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    kc, vc = oracle_after_store(h)
+    ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
+                        nthreads=ORACLE_THREADS)
+    compare(out, ref, f"decode crossover batch {batch}")
+
+
 FUSED_CASES = [
     # (block_size, Hq, Hkv, lengths): ragged tails, padding rows, pairs cut many times
     (16, 32, 8, [1, 15, 16, 17, 255, 256, 257, 600, 1023, 0, 2048, 333]),
