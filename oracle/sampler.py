@@ -104,7 +104,9 @@ def sample(probs, seed, offset, rows=None):
     B, V = p.shape
     rows = np.arange(B) if rows is None else np.asarray(rows)
     u = uniforms(row_bits(rows, V, seed, offset))
-    e32 = -np.log2(u)                          # float32
+    # E = -log2(u) taken in fp64 and rounded once to fp32: exactly rounded
+    # (numpy's own fp32 log2 carries no such guarantee).
+    e32 = (-np.log2(u.astype(np.float64))).astype(np.float32)
     key32 = p / e32                            # float32, correctly rounded division
     tok = np.argmax(key32, axis=1).astype(np.int32)
     key64 = p.astype(np.float64) / -np.log2(u.astype(np.float64))
