@@ -159,7 +159,7 @@ def run_timed(step, warmup, steps, warm_s=0.0):
     return ms, [a.elapsed_time(b) for a, b in evs]
 
 
-def decode_bench(name, warmup, steps, fused=True, warm_s=0.0):
+def decode_bench(name, warmup, steps, fused=True, warm_s=0.0, flushed_only=False):
     import torch
     import numpy as np
     import paged_kv_cache_slot_amd as pa
@@ -170,6 +170,9 @@ def decode_bench(name, warmup, steps, fused=True, warm_s=0.0):
     ws = torch.empty(pa.pa_decode_workspace_bytes(B, hq, d, case["max_context_len"],
                                                   case["block_size"]),
                      dtype=torch.uint8, device="cuda")
+    # The buffer that evicts the 256 MB last-level cache (MALL) before each
+    # call of the flushed protocol, allocated before anything is timed.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
     def step(i, ev):
@@ -191,19 +194,20 @@ def decode_bench(name, warmup, steps, fused=True, warm_s=0.0):
         if ev:
             ev[1].record()
 
-    ms, kms = run_timed(step, warmup, steps, warm_s)
-    # The same call again with the 256 MB last-level cache (MALL) overwritten
-    # before each one (a 512 MiB fill outside the timed events), so that no
-    # part of the pool can be served from it: median of the decode calls.
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    evs = []
-    for i in range(steps):
+    def flushed_step(i, ev):
+        # The survey's protocol: a 512 MiB write before every call (outside
+        # its events), so no part of the pool is served from the MALL.
         scratch.fill_(i & 0xFF)
-        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         step(i, ev)
-        evs.append(ev)
-    torch.cuda.synchronize()
-    flushed_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    if flushed_only:  # the flushed loop alone (for a kernel trace of it)
+        _, fk = run_timed(flushed_step, warmup, steps, warm_s)
+        return dict(flushed_ms=float(np.median(fk)), flushed_all_ms=fk)
+    ms, kms = run_timed(step, warmup, steps, warm_s)
+    # The same call under the flushed protocol, warmed up the same way and
+    # with the garbage collector paused: median of the decode calls.
+    _, fk = run_timed(flushed_step, warmup, steps, warm_s)
+    flushed_ms = float(np.median(fk))
     del scratch
     # Bytes of the timed call: the decode's, plus the fused store's writes.
     dbytes = decode_bytes(case) + (store_bytes(case, fused=True) if fused else 0)
@@ -214,7 +218,8 @@ def decode_bench(name, warmup, steps, fused=True, warm_s=0.0):
                decode_gbs=dbytes / (kern_ms * 1e-3) / 1e9, flushed_ms=flushed_ms,
                decode_ms_min=float(np.min(kms)), decode_ms_median=float(np.median(kms)),
                decode_ms_max=float(np.max(kms)),
-               flushed_gbs=dbytes / (flushed_ms * 1e-3) / 1e9)
+               flushed_gbs=dbytes / (flushed_ms * 1e-3) / 1e9,
+               flushed_ms_min=float(np.min(fk)), flushed_ms_max=float(np.max(fk)))
     return res
 
 
@@ -439,7 +444,9 @@ def cpu_baseline(case):
     import numpy as np
     import torch
     import oracle
-    nthreads = min(oracle.hardware_threads(), len(os.sched_getaffinity(0)), 16)
+    hw = oracle.hardware_threads()
+    affinity = len(os.sched_getaffinity(0))
+    nthreads = min(hw, affinity, 16)
     u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     kc, vc = u16(case["k_cache"]), u16(case["v_cache"])
     kn, vn = u16(case["k_new"]), u16(case["v_new"])
@@ -453,6 +460,9 @@ def cpu_baseline(case):
     nbytes = decode_bytes(case) + store_bytes(case)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
             "kind": "oracle", "seconds": round(dt, 3),
+            "host": {"nproc": os.cpu_count(), "hardware_concurrency": hw,
+                     "affinity_cpus": affinity,
+                     "threads_used": f"min(hardware_concurrency, affinity, 16) = {nthreads}"},
             "sample": f"the whole step once: store of {case['batch']} new tokens + fp64 "
                       f"attention for all {case['batch']} rows x {case['num_q_heads']} heads "
                       f"(qwen3_0.6b_decode, {int(np.asarray(case['lens']).sum())} context tokens)"}
@@ -465,9 +475,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-leg", choices=["prefill", "sampler"], default=None,
-                    help="only run this leg and print its own result (for counter runs under "
-                         "rocprofv3); the benchmark line is not printed")
+    ap.add_argument("--profile-leg", choices=["prefill", "sampler", "decode", "decode-flushed"],
+                    default=None,
+                    help="only run this leg and print its own result (for counter runs and "
+                         "kernel traces under rocprofv3); the benchmark line is not printed")
+    ap.add_argument("--workload", default="qwen3_0.6b_decode",
+                    help="decode workload of --profile-leg decode / decode-flushed")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (a known "
                          "byte count for scaling the HBM counters of rocprofv3)")
@@ -493,9 +506,17 @@ def main():
     if args.profile_leg:
         fn = {"prefill": lambda: prefill_bench(max(args.warmup, SECONDARY_WARMUP), args.steps,
                                                warm_s=SECONDARY_WARM_S),
-              "sampler": lambda: sampler_bench(args.warmup, args.steps)}[args.profile_leg]
+              "sampler": lambda: sampler_bench(args.warmup, args.steps),
+              "decode": lambda: decode_bench(args.workload, max(args.warmup, SECONDARY_WARMUP),
+                                             args.steps, warm_s=SECONDARY_WARM_S),
+              "decode-flushed": lambda: decode_bench(args.workload,
+                                                     max(args.warmup, SECONDARY_WARMUP),
+                                                     args.steps, warm_s=SECONDARY_WARM_S,
+                                                     flushed_only=True)}[args.profile_leg]
         res = fn()
-        print(json.dumps({k: v for k, v in res.items() if k != "case"}), flush=True)
+        print(json.dumps({k: v for k, v in res.items() if k != "case"},
+                         default=lambda x: x.tolist() if hasattr(x, "tolist") else str(x)),
+              flush=True)
         return
     log(f"device: {torch.cuda.get_device_name(0)} "
         f"({torch.cuda.get_device_properties(0).gcnArchName})")
@@ -512,8 +533,12 @@ def main():
                 "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": main_res["decode_bytes"],
                 "avg_launch_us": round(main_res["decode_ms"] * 1e3, 2),
+                "median_launch_us": round(main_res["decode_ms_median"] * 1e3, 2),
                 "mall_flushed_median_us": round(main_res["flushed_ms"] * 1e3, 2),
                 "mall_flushed_frac": round(main_res["flushed_gbs"] / HBM_PEAK_GBS, 4),
+                "protocol": "frac: mean of back-to-back calls (HIP events); mall_flushed_*: "
+                            "median with a 512 MiB write before every call (the survey's "
+                            "protocol)",
                 "source_digest": digest}
 
     secondary = []
@@ -528,6 +553,7 @@ def main():
                 "decode_us": round(r["decode_ms"] * 1e3, 2),
                 "decode_GBps": round(r["decode_gbs"], 2),
                 "decode_frac_hbm": round(r["decode_gbs"] / HBM_PEAK_GBS, 4),
+                "decode_median_us": round(r["decode_ms_median"] * 1e3, 2),
                 "mall_flushed_median_us": round(r["flushed_ms"] * 1e3, 2),
                 "mall_flushed_frac": round(r["flushed_gbs"] / HBM_PEAK_GBS, 4)})
             del r

@@ -62,7 +62,8 @@ extern "C" {
 #define PA_ERR_NO_BLOCKS (-6)   /* block manager: not enough free blocks        */
 #define PA_ERR_SEQ (-7)         /* block manager: sequence id unknown or in use */
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL). [not on the pages: library
+ * plumbing, no operation of the method] */
 const char* pa_status_string(int status);
 
 /*
@@ -91,6 +92,8 @@ int pa_store_kvcache(const void* k, const void* v, int64_t kv_token_stride,
                      int32_t num_kv_heads, int32_t head_dim, void* stream);
 
 /*
+ * [not on the pages: the pages give no split of a long context across the
+ * GPU; this sizes the split-K partials of pa_decode's own design.]
  * Bytes of device workspace pa_decode needs for these sizes: a small header,
  * then per working wavefront the merge job of the boundary where its range of
  * the work starts, and two partial (acc, max, sum) records per query head,
@@ -203,6 +206,8 @@ int pa_prefill_varlen(void* out, const void* q, const void* k_cache,
 
 /*
  * pa_validate_metadata -- host-side check of the metadata contract.
+ * [not on the pages: a test aid; the pages state the metadata (block table,
+ * slot_mapping with -1) but no checks of it.]
  * All pointers are HOST arrays; nothing touches the GPU. Checks that every
  * context length is in [0, max_context_len] (max_context_len < 0 skips that
  * bound), that every block-table entry a row reads is in [0, num_blocks), that

@@ -21,10 +21,12 @@
 // reads below hit distinct LDS banks.
 //
 // Per wavefront and tile, flash-attention style, in log2 units:
-//   Q' = Q * scale * log2(e), rounded to bf16 once per work-group;
-//   S^T = K Q'^T     bf16 MFMA 32x32x16, fp32 accumulate: each lane holds the
+//   S^T = K Q^T      bf16 MFMA 32x32x16, fp32 accumulate: each lane holds the
 //                    scores of ONE query row, so row reductions stay in-lane
 //                    except for one exchange with the lane 32 apart;
+//   s = S * scale * log2(e) in fp32 (one fma per score, which also subtracts
+//                    the reference below): the scale is never rounded into a
+//                    bf16 operand, whose error would grow with |S|;
 //   p = 2^(s - mc)   against a per-row reference mc, set from the first
 //                    tile's row maximum and raised (rescaling the output) only
 //                    when a tile's per-lane row sum of p exceeds 256, so no
@@ -178,15 +180,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int wave_pos0 = P + tok0 + (wave * 32) % TQ;    // lowest position of the wavefront's rows
   const int wave_pos1 = wave_pos0 + min(32, TQ) - 1;    // highest
 
-  // Q of this lane's row (loaded here, converted below once tile 0's copy is
-  // in flight too, so the two latencies overlap).
-  uint4 qraw[kHeadDim / 16];
-  bf16x8_t qreg[kHeadDim / 16];  // filled once tile 0 is requested
+  // Q of this lane's row, the B operand of the score MFMAs as it is.
+  bf16x8_t qreg[kHeadDim / 16];
   {
     const uint16_t* qp = q + (static_cast<int64_t>(qt) * num_q_heads + head) * kHeadDim + half * 8;
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 16; ++ks)
-      qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 16);
+      qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
   }
 
   f32x16_t o[kHeadDim / 32];
@@ -195,15 +195,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   // Softmax state of this lane's row, in log2 units: mc is the reference the
-  // exponentials are taken against, p = 2^(s - mc). The score MFMAs start from
-  // -mc (minit), so their output is s - mc directly. mc is set from the first
+  // exponentials are taken against, p = 2^(s - mc). mc is set from the first
   // tile's row maximum and afterwards raised only when a tile's row sum of p
   // exceeds kRescaleSum, which keeps every p below that bound; the final
   // o / lsum is the same for any reference.
   float mc = 0.f;
-  f32x16_t minit;
+  f32x16_t zero16;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) minit[r] = 0.f;
+  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
   float lsum = 0.f;
 
   const int bs_mask = (1 << log2_bs) - 1;
@@ -297,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     // Issue priority: raised while this wavefront feeds the matrix core, so
     // that the other wavefront on the SIMD runs its softmax in the gaps.
     __builtin_amdgcn_s_setprio(1);
-    f32x16_t s[2] = {minit, minit};
+    f32x16_t s[2] = {zero16, zero16};
     bf16x8_t ka[3][2];
     ka[0][0] = read_k(0, 0);
     ka[0][1] = read_k(1, 0);
@@ -321,6 +320,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     }
     sched_group(kSchedMfma, 4);
     __builtin_amdgcn_s_setprio(0);
+
+    // Scaled scores in log2 units, relative to the reference.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], scale_log2, -mc);
 
     // Mask (lane holds keys kb*32 + (r/4)*8 + half*4 + r%4 of the tile).
     if (masked) {  // one uniform branch around the whole mask
@@ -379,8 +384,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] -= d;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) minit[r] = -mc;
       make_p();
     };
     make_p();
@@ -454,18 +457,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   };
   issue_tile(0, block_of(0), lds_k0, lds_v0);
   blk_next = block_of(1);
-
-  // Q pre-multiplied by scale * log2(e) and rounded to bf16 once, so the
-  // scores come out of the MFMA in log2 units.
-#pragma unroll
-  for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-    const uint32_t w[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
-    uint32_t sw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sw[i] = pack_bf16x2(bf16_lo(w[i]) * scale_log2, bf16_hi(w[i]) * scale_log2);
-    qreg[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(sw[0], sw[1], sw[2], sw[3]));
-  }
 
   for (int t = 0; t < num_tiles; t += 2) {
     step(t, lds_k0, lds_v0, lds_k1, lds_v1);

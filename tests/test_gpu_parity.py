@@ -14,7 +14,7 @@ import oracle
 import paged_kv_cache_slot_amd as pa
 import workloads
 from tests.gpu_common import (DEV, compare, gpu_decode, gpu_prefill, gpu_store, host_copy,
-                              make_case, oracle_after_store, require_gpu, sample_rows, say,
+                              make_case, oracle_after_store, require_gpu, say,
                               ORACLE_THREADS)
 
 pytestmark = pytest.mark.gpu
@@ -83,23 +83,45 @@ def test_store_empty_is_noop():
 @pytest.mark.parametrize("name", ["tiny_decode", "qwen3_0.6b_decode", "qwen3_8b_decode",
                                   "bs16_stress_decode"])
 def test_decode_step_full_size(name):
-    """store + decode on the full workload; every row for the tiny workload, sampled rows
-    (longest, shortest, padding, 40 random) for the others."""
+    """The decode step on the full workload, both ways it can be called: the
+    fused pa_decode_store (the call the benchmark times) and pa_store_kvcache
+    followed by pa_decode. Every row of both outputs against the oracle, both
+    pools bit for bit against the oracle's store after each, and the two
+    outputs bit for bit against each other."""
     case, h = make_case(name)
-    say(f"  pa_store_kvcache + pa_decode B={case['batch']} Hq={case['num_q_heads']} "
-        f"Hkv={case['num_kv_heads']} bs={case['block_size']} max_len={case['max_context_len']}")
-    gpu_store(case)
-    out = gpu_decode(case)
+    B, hq, d = case["q"].shape
+    say(f"  pa_decode_store B={case['batch']} Hq={case['num_q_heads']} "
+        f"Hkv={case['num_kv_heads']} bs={case['block_size']} max_len={case['max_context_len']} "
+        f"(-1 slots: {int((h['slot_mapping'] < 0).sum())})")
+    ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(B, hq, d, case["max_context_len"],
+                                                          case["block_size"])),
+                     dtype=torch.uint8, device=DEV)
+    fused = torch.full_like(case["q"], float("nan"))
+    pa.pa_decode_store(fused, case["q"], case["k_new"], case["v_new"], case["k_cache"],
+                       case["v_cache"], case["slot_mapping"], case["block_table"],
+                       case["context_lens"], case["max_context_len"], case["scale"], ws)
     torch.cuda.synchronize()
     kc, vc = oracle_after_store(h)
-    rows = None if name == "tiny_decode" else sample_rows(h["lens"], 40,
-                                                          seed=workloads.seed_of(name))
+    assert np.array_equal(_pool_bits(case["k_cache"]), kc), "fused: K pool differs from the oracle"
+    assert np.array_equal(_pool_bits(case["v_cache"]), vc), "fused: V pool differs from the oracle"
     ref = oracle.decode(h["q"], kc, vc, h["block_table"], h["context_lens"], h["scale"],
-                        rows=rows, nthreads=ORACLE_THREADS)
-    compare(out, ref, f"{name} decode", rows=rows)
+                        nthreads=ORACLE_THREADS)
+    compare(fused, ref, f"{name} pa_decode_store, every row")
     pad = np.flatnonzero(h["lens"] == 0)
     if len(pad):
-        assert int(out[torch.from_numpy(pad).to(DEV)].float().abs().sum()) == 0
+        assert int(fused[torch.from_numpy(pad).to(DEV)].float().abs().sum()) == 0
+
+    # The same step as two calls, from the pre-store pools.
+    case["k_cache"].copy_(h["k_cache"])
+    case["v_cache"].copy_(h["v_cache"])
+    say("  pa_store_kvcache + pa_decode")
+    gpu_store(case)
+    sep = gpu_decode(case)
+    torch.cuda.synchronize()
+    assert np.array_equal(_pool_bits(case["k_cache"]), kc), "store: K pool differs from the oracle"
+    assert np.array_equal(_pool_bits(case["v_cache"]), vc), "store: V pool differs from the oracle"
+    compare(sep, ref, f"{name} pa_store_kvcache + pa_decode, every row")
+    assert torch.equal(sep, fused), "fused and separate decode steps differ"
 
 
 DECODE_GRID = [
@@ -352,9 +374,29 @@ def test_decode_deterministic():
 
 # ---------------------------------------------------------------- prefill --
 
-def test_prefill_full_size_sampled():
-    """Config 4 (64 sequences, cached prefixes from 8 shared chains): store the
-    new tokens, run prefill, check 160 sampled query rows (all heads)."""
+def _whole_sequences(h, extra, seed):
+    """Sequences to check in full: the longest, the longest of each prefix
+    length (0 .. 3 blocks), and `extra` more drawn at random."""
+    N = np.asarray(h["new_lens"])
+    k = np.asarray(h["prefix_blocks"])
+    pick = {int(np.argmax(N))}
+    for kb in range(int(k.max()) + 1):
+        cand = np.flatnonzero(k == kb)
+        if len(cand):
+            pick.add(int(cand[np.argmax(N[cand])]))
+    rng = np.random.default_rng(seed)
+    rest = [b for b in range(len(N)) if b not in pick]
+    pick |= set(int(b) for b in rng.choice(rest, size=min(extra, len(rest)), replace=False))
+    return sorted(pick)
+
+
+def test_prefill_full_size():
+    """The Qwen3-8B prefill workload (64 sequences, cached prefixes from 8
+    shared chains): store the new tokens, run prefill, then check every row and
+    head of whole sequences -- the longest, the longest with each prefix length
+    0..3 blocks, two more -- so that every query tile and key tile of those
+    sequences is compared, plus 120 rows drawn from the whole batch and the
+    first and last row of 10 more sequences."""
     case, h = make_case("qwen3_8b_prefill_prefix")
     say(f"  pa_store_kvcache + pa_prefill_varlen T={case['total_q']} "
         f"max_seqlen_q={case['max_seqlen_q']}")
@@ -362,15 +404,22 @@ def test_prefill_full_size_sampled():
     out = gpu_prefill(case)
     torch.cuda.synchronize()
     kc, vc = oracle_after_store(h)
-    rng = np.random.default_rng(44)
     cu = h["cu_seqlens_q"].numpy()
-    toks = set(int(x) for x in rng.choice(case["total_q"], size=120, replace=False))
+    seqs = _whole_sequences(h, 2, seed=45)
+    toks = set()
+    for b in seqs:
+        toks |= set(range(int(cu[b]), int(cu[b + 1])))
+    say(f"  whole sequences {seqs}: new lengths {[int(h['new_lens'][b]) for b in seqs]}, "
+        f"prefix blocks {[int(h['prefix_blocks'][b]) for b in seqs]}")
+    rng = np.random.default_rng(44)
+    toks |= set(int(x) for x in rng.choice(case["total_q"], size=120, replace=False))
     for b in rng.choice(case["batch"], size=10, replace=False):   # first and last rows
         toks |= {int(cu[b]), int(cu[b + 1] - 1)}
     toks = np.array(sorted(toks), dtype=np.int32)
+    say(f"  {len(toks)} query rows of {case['total_q']} checked, all {case['num_q_heads']} heads")
     ref = oracle.prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["context_lens"], h["block_table"],
                          h["scale"], tokens=toks, nthreads=ORACLE_THREADS)
-    compare(out, ref, "qwen3_8b_prefill_prefix prefill", rows=toks)
+    compare(out, ref, "qwen3_8b_prefill_prefix prefill (whole sequences + sample)", rows=toks)
 
 
 PREFILL_GRID = [
@@ -430,11 +479,14 @@ def test_prefill_sequences_without_new_tokens():
     assert out.shape[0] == 0
 
 
-def test_prefill_row_matches_gpu_decode():
-    """Prefill row i of a sequence with prefix P equals decode with L = P + i + 1."""
+def test_prefill_row_matches_decode():
+    """Prefill row i of a sequence with prefix P and decode with L = P + i + 1
+    over the same pool compute the same attention: both against the oracle's
+    decode for those lengths, and the oracle's prefill and decode agree."""
     case = workloads.prefill_case(1, (1, 1024), 32, 8, 128, 16, seed=61, device=DEV, chains=1,
                                   chain_blocks=3, new_lens=[150], prefix_blocks=[3],
                                   prefix_chain=[0])
+    h = host_copy(case)
     gpu_store(case)
     pre = gpu_prefill(case)
     P = 48
@@ -446,8 +498,17 @@ def test_prefill_row_matches_gpu_decode():
                     max_context_len=P + 150)
     dec = gpu_decode(dec_case)
     torch.cuda.synchronize()
-    diff = (pre[rows].float() - dec.float()).abs()
-    assert float(diff.max()) <= 2e-2, float(diff.max())
+    kc, vc = oracle_after_store(h)
+    ref_dec = oracle.decode(h["q"][rows], kc, vc,
+                            np.repeat(h["block_table"].numpy(), len(rows), axis=0),
+                            np.array([P + i + 1 for i in rows], dtype=np.int32), h["scale"],
+                            nthreads=ORACLE_THREADS)
+    ref_pre = oracle.prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["context_lens"],
+                             h["block_table"], h["scale"], tokens=np.array(rows, np.int32),
+                             nthreads=ORACLE_THREADS)[rows]
+    assert np.array_equal(ref_pre, ref_dec)
+    compare(pre[rows], ref_dec, "prefill rows against the oracle's decode")
+    compare(dec, ref_dec, "decode at L = P + i + 1 against the oracle")
 
 
 def test_prefill_shared_prefix_rows_identical():
