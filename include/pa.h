@@ -61,6 +61,7 @@ extern "C" {
 #define PA_ERR_HIP (-5)         /* the HIP runtime reported an error on launch  */
 #define PA_ERR_NO_BLOCKS (-6)   /* block manager: not enough free blocks        */
 #define PA_ERR_SEQ (-7)         /* block manager: sequence id unknown or in use */
+#define PA_ERR_SCRATCH (-8)     /* pa_decode_store_noalloc: beyond its scratch   */
 
 /* Static text for a status code (never NULL). [not on the pages: library
  * plumbing, no operation of the method] */
@@ -173,6 +174,33 @@ int pa_decode_store(void* out, const void* q, const void* k_new, const void* v_n
                     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads,
                     int32_t head_dim, int32_t block_size, int32_t max_context_len, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_store_noalloc -- pa_decode_store without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ *   Same arguments, result (output and pools, bit for bit) and errors as
+ *   pa_decode_store, minus workspace/workspace_bytes. The split-K records live
+ *   in a file-scope device array of 16 MiB inside libpa.so, one copy per GPU,
+ *   held until the process ends; the call allocates nothing (no hipMalloc,
+ *   hipFree or allocating library routine), and its first call on a device
+ *   looks up that device's copy (hipGetSymbolAddress) and keeps the address.
+ *   A call needing more scratch than 16 MiB returns PA_ERR_SCRATCH and
+ *   enqueues nothing; on a 256-CU MI355X every batch, head count and context
+ *   length fits (at most ~8.7 MB is used: the records are bounded by the
+ *   launch grid, one work-group per compute unit). Every call on one GPU
+ *   shares that GPU's array, so calls that overlap on one GPU (concurrent
+ *   streams, or host threads without ordering) race; calls ordered on one
+ *   stream do not. Nothing in the array needs clearing between calls.
+ */
+int pa_decode_store_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                            int64_t kv_token_stride, void* k_cache, void* v_cache,
+                            const int32_t* slot_mapping, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* context_lens,
+                            int32_t batch, int32_t num_blocks, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t max_context_len, float scale, void* stream);
 
 /*
  * pa_prefill_varlen -- causal attention for a batch of variable-length

@@ -688,7 +688,56 @@ int launch_split(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
   return nb;
 }
 
+// The scratch of the no-allocation decode entry point (pa_decode_store_noalloc):
+// a file-scope device array, one copy per device, held until the process
+// ends. Host code never passes its name to a kernel: on the host the name is
+// a stand-in, not a device address; decode_scratch() returns the address
+// hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+// Bound on the workspace bytes one launch of decode_kernel<G, CH> + its merge
+// touches on the current device: nw <= grid * W working wavefronts, grid <=
+// the resident work-groups; the merge reads job records of up to
+// grid * W + kMergeWaves - 1 boundaries (those past nw are ignored).
+template <int G, int CH>
+size_t grid_workspace_bound() {
+  const int64_t waves = static_cast<int64_t>(resident_groups<G, CH>()) * decode_waves<G>();
+  return std::max(partial_offset(waves + kMergeWaves),
+                  partial_offset(waves) +
+                      static_cast<size_t>(2 * waves * G) * kRecord * sizeof(float));
+}
+
 }  // namespace
+
+size_t decode_scratch_need(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t max_context_len) {
+  size_t grid = 0;
+  switch (num_q_heads / num_kv_heads) {
+    case 1: grid = grid_workspace_bound<1, 4>(); break;
+    case 2: grid = grid_workspace_bound<2, 4>(); break;
+    case 4: grid = grid_workspace_bound<4, 4>(); break;
+    case 8: grid = grid_workspace_bound<8, 2>(); break;
+    default: return 0;
+  }
+  return std::min(grid, decode_workspace_bytes(batch, num_q_heads, max_context_len));
+}
+
+hipError_t decode_scratch(void** ptr) {
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 void prepare_decode(int32_t num_q_heads, int32_t num_kv_heads) {
   switch (num_q_heads / num_kv_heads) {

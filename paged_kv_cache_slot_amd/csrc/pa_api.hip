@@ -61,6 +61,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_HIP: return "HIP launch error";
     case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
     case PA_ERR_SEQ: return "sequence id unknown or already live";
+    case PA_ERR_SCRATCH:
+      return "the call needs more than the fixed 16 MiB device scratch of "
+             "pa_decode_store_noalloc";
     default: return "unknown status";
   }
 }
@@ -153,6 +156,47 @@ int pa_decode_store(void* out, const void* q, const void* k_new, const void* v_n
       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table,
       block_table_stride, context_lens, batch, num_q_heads, num_kv_heads, block_size,
       max_context_len, scale, workspace, fs, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode_store_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                            int64_t kv_token_stride, void* k_cache, void* v_cache,
+                            const int32_t* slot_mapping, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* context_lens,
+                            int32_t batch, int32_t num_blocks, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t max_context_len, float scale, void* stream) {
+  if (batch < 0 || num_blocks < 0 || max_context_len < 0 || block_table_stride < 0 ||
+      !valid_scale(scale))
+    return PA_ERR_SHAPE;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (static_cast<int64_t>(block_table_stride) * block_size < max_context_len)
+    return PA_ERR_SHAPE;
+  if (kv_token_stride < static_cast<int64_t>(num_kv_heads) * head_dim) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !slot_mapping || !block_table ||
+      !context_lens)
+    return PA_ERR_NULL;
+  if (kv_token_stride % 8 != 0 || !aligned16(out) || !aligned16(q) || !aligned16(k_new) ||
+      !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  if (pa::decode_scratch_need(batch, num_q_heads, num_kv_heads, max_context_len) >
+      pa::kDecodeScratchBytes)
+    return PA_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (pa::decode_scratch(&scratch) != hipSuccess) return PA_ERR_HIP;
+  pa::FusedStore fs;
+  fs.k_new = static_cast<const uint16_t*>(k_new);
+  fs.v_new = static_cast<const uint16_t*>(v_new);
+  fs.kv_stride = kv_token_stride;
+  fs.slot_mapping = slot_mapping;
+  fs.k_store = static_cast<uint16_t*>(k_cache);
+  fs.v_store = static_cast<uint16_t*>(v_cache);
+  return from_hip(pa::launch_decode(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table,
+      block_table_stride, context_lens, batch, num_q_heads, num_kv_heads, block_size,
+      max_context_len, scale, scratch, fs, static_cast<hipStream_t>(stream)));
 }
 
 int pa_prefill_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -46,6 +46,21 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
 
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_context_len);
 
+// Fixed device scratch of the decode entry point that allocates nothing: a
+// file-scope device array of this many bytes, one copy per device.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+
+// Bytes of that scratch a decode of these sizes uses on the current device:
+// the smaller of decode_workspace_bytes and the bound set by the launch grid,
+// which never exceeds one work-group per resident slot of the device.
+size_t decode_scratch_need(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t max_context_len);
+
+// Device address of the scratch array on the current device, looked up once
+// per device with hipGetSymbolAddress (the array's name is only a host-side
+// stand-in) and kept.
+hipError_t decode_scratch(void** ptr);
+
 size_t sample_workspace_bytes(int32_t batch, int32_t vocab);
 
 hipError_t launch_sample(int32_t* tokens, const float* probs, int64_t row_stride, int32_t batch,

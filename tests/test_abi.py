@@ -46,7 +46,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, -5, -6, -7):
+    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, -5, -6, -7,
+                 -8):
         assert pa.pa_status_string(code) not in ("", "unknown status")
     assert pa.pa_status_string(1234) == "unknown status"
 
@@ -121,6 +122,29 @@ def test_decode_store_argument_checks(lib):
     assert call(wsb=ws - 1) == PA_ERR_WORKSPACE
     assert call(ws=None) == PA_ERR_WORKSPACE
     for bad in (0.0, -0.088, float("nan"), float("inf")):
+        assert call(scale=bad) == PA_ERR_SHAPE
+
+
+def test_decode_store_noalloc_argument_checks(lib):
+    f = lib.pa_decode_store_noalloc
+    P = _fake()
+    base = dict(out=P, q=P, kn=P, vn=P, kvs=1024, kc=P, vc=P, sm=P, bt=P, stride=2, cl=P, B=4,
+                nb=10, hq=16, hkv=8, d=128, bs=256, maxl=300, scale=0.088)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["out"], a["q"], a["kn"], a["vn"], a["kvs"], a["kc"], a["vc"], a["sm"], a["bt"],
+                 a["stride"], a["cl"], a["B"], a["nb"], a["hq"], a["hkv"], a["d"], a["bs"],
+                 a["maxl"], a["scale"], None)
+
+    assert call(B=0) == PA_OK
+    for name in ("out", "q", "kn", "vn", "kc", "vc", "sm", "bt", "cl"):
+        assert call(**{name: None}) == PA_ERR_NULL, name
+    assert call(kvs=1000) == PA_ERR_SHAPE
+    assert call(kvs=1028) == PA_ERR_UNSUPPORTED
+    assert call(hq=24, hkv=8) == PA_ERR_UNSUPPORTED
+    assert call(stride=1) == PA_ERR_SHAPE
+    for bad in (0.0, float("nan")):
         assert call(scale=bad) == PA_ERR_SHAPE
 
 
