@@ -337,24 +337,24 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
 
   // ---- one chunk: loads, then arithmetic ------------------------------------
   // Chunk c of a segment covers tokens t0 + T*c .. t0 + T*c + T - 1; row grp of
-  // lanes takes token (first + 4j + grp) for j < CH. Groups past the segment
-  // re-read the chunk's first token (cached), tokens past it inside the last
-  // group re-read token tend-1 of the same block, and a chunk with no tokens at
-  // all reads the segment's q row.
+  // lanes takes token (first + 4j + grp) for j < CH. Groups past the segment,
+  // a chunk with no tokens at all, and every chunk of an invalid segment read
+  // the segment's q row instead (a few hundred bytes the wavefront has just
+  // loaded); tokens past it inside the last group re-read token tend-1 in the
+  // same instruction as the lane that needs it.
   auto issue = [&](const Seg& it, int my_blk, int ns, int c, uint4 (&kb)[CH],
                    uint4 (&vb)[CH]) {
     const int cbase = it.t0 + c * T;
-    const bool active = cbase < it.tend;  // uniform
+    // Uniform. An invalid segment (the prefetch past the end of the range)
+    // carries the fields of a real one, so that its stand-in loads have
+    // valid addresses; it loads nothing of the pool.
+    const bool active = it.valid && cbase < it.tend;
     // The new token's row comes from k_new/v_new when this chunk holds it.
     const int new_tok = ns >= 0 && cbase + T > it.L - 1 ? it.L - 1 : -1;
     const int64_t new_off = static_cast<int64_t>(it.b) * kv_stride + it.g * kHeadDim + sub * 8;
     const int bidx0 = it.t0 >> log2_bs;
     const int ngroups = min(CH, (it.tend - cbase + 3) >> 2);
     const int64_t head_off = it.g * kHeadDim + sub * 8;
-    const int blk0 = __builtin_amdgcn_readlane(my_blk, (cbase >> log2_bs) - bidx0);
-    const int64_t off0 =
-        ((static_cast<int64_t>(blk0) << log2_bs) | (min(cbase + grp, it.tend - 1) & bs_mask)) *
-            slot_stride + head_off;
     const uint16_t* dummy = q_row(it) + zero;
     const uint16_t* kp[CH];
     const uint16_t* vp[CH];
@@ -365,10 +365,10 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
       const int tc = min(tw + grp, it.tend - 1);
       const int64_t o =
           ((static_cast<int64_t>(blk) << log2_bs) | (tc & bs_mask)) * slot_stride + head_off;
-      const int64_t off = j < ngroups ? o : off0;
       const bool fresh = active && tc == new_tok;
-      kp[j] = fresh ? k_new + new_off : (active ? k_cache + off : dummy);
-      vp[j] = fresh ? v_new + new_off : (active ? v_cache + off : dummy);
+      const bool real = active && j < ngroups;
+      kp[j] = fresh ? k_new + new_off : (real ? k_cache + o : dummy);
+      vp[j] = fresh ? v_new + new_off : (real ? v_cache + o : dummy);
     }
 #pragma unroll
     for (int j = 0; j < CH; ++j) kb[j] = load_stream(kp[j]);
