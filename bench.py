@@ -475,12 +475,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-leg", choices=["prefill", "sampler", "decode", "decode-flushed"],
+    ap.add_argument("--profile-leg", choices=["prefill", "sampler", "decode", "decode-flushed",
+                                              "graphs"],
                     default=None,
                     help="only run this leg and print its own result (for counter runs and "
                          "kernel traces under rocprofv3); the benchmark line is not printed")
     ap.add_argument("--workload", default="qwen3_0.6b_decode",
                     help="decode workload of --profile-leg decode / decode-flushed")
+    ap.add_argument("--batch", type=int, default=256,
+                    help="batch of --profile-leg graphs (eager and graph steps at that batch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (a known "
                          "byte count for scaling the HBM counters of rocprofv3)")
@@ -512,7 +515,8 @@ def main():
               "decode-flushed": lambda: decode_bench(args.workload,
                                                      max(args.warmup, SECONDARY_WARMUP),
                                                      args.steps, warm_s=SECONDARY_WARM_S,
-                                                     flushed_only=True)}[args.profile_leg]
+                                                     flushed_only=True),
+              "graphs": lambda: graph_bench(batches=(args.batch,))}[args.profile_leg]
         res = fn()
         print(json.dumps({k: v for k, v in res.items() if k != "case"},
                          default=lambda x: x.tolist() if hasattr(x, "tolist") else str(x)),
