@@ -35,7 +35,7 @@
 //                    accumulators (converted to bf16) and V^T built by
 //                    ds_read_b64_tr_b16 transposed reads from the row-major V
 //                    tile, with keys ordered to match the accumulator layout;
-//                    the row sum adds the same bf16 values (v_dot2 with ones).
+//                    the row sum adds the fp32 exponentials.
 // Tiles wholly above the causal diagonal are skipped per wavefront; tiles
 // wholly below it skip the mask.
 //
@@ -73,7 +73,6 @@ __device__ __forceinline__ int swz(int key) { return ((key << 1) & 14) | ((key >
 // Largest per-lane share of a tile's row sum of exponentials before the row's
 // reference is raised; every exponential stays below it.
 constexpr float kRescaleSum = 256.f;
-constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;  // (1.0, 1.0) in bf16
 
 // v_permlane32_swap of x with itself: the first result holds the low half's
 // values in both halves, the second the high half's, so a symmetric
@@ -339,29 +338,30 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     __builtin_amdgcn_s_setprio(1);
 
     // P = 2^(s - mc) in bf16 as the B operand, 16 keys per MFMA step; tsum is
-    // this lane's share of the tile's row sum, over the same bf16 values that
-    // enter the product.
+    // this lane's share of the tile's row sum, added in fp32 from the
+    // exponentials before they are rounded to bf16. (Plain adds, not v_dot2:
+    // the dot instructions do not issue while the matrix core is busy, fp32
+    // adds do, beside the other wavefront's MFMAs.)
     bf16x8_t pb[4];
     float tsum;
     auto make_p = [&]() {
-      float t0 = 0.f, t1 = 0.f;
+      float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          uint32_t w[4];
+          float e[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            w[i] = pack_bf16x2(fast_exp2(s[kb][hs * 8 + 2 * i]),
-                               fast_exp2(s[kb][hs * 8 + 2 * i + 1]));
-          t0 = dot2_bf16(w[0], kOnesBf16x2, t0);
-          t1 = dot2_bf16(w[1], kOnesBf16x2, t1);
-          t0 = dot2_bf16(w[2], kOnesBf16x2, t0);
-          t1 = dot2_bf16(w[3], kOnesBf16x2, t1);
-          pb[kb * 2 + hs] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+          for (int i = 0; i < 8; ++i) {
+            e[i] = fast_exp2(s[kb][hs * 8 + i]);
+            t[i & 3] += e[i];
+          }
+          pb[kb * 2 + hs] = __builtin_bit_cast(
+              bf16x8_t, make_uint4(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                                   pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])));
         }
       }
-      tsum = t0 + t1;
+      tsum = (t[0] + t[1]) + (t[2] + t[3]);
     };
     // Moves the reference up to the row maximum where that is higher (to it in
     // any case on the first tile), rescales the state and recomputes P.
