@@ -158,9 +158,9 @@ int pa_decode(void* out, const void* q, const void* k_cache,
  *   context_lens[b] - 1 (the new token), or -1 when that token is already in
  *   the pool; for a padding row (context_lens[b] == 0) it is -1. Other
  *   layouts are undefined (the separate calls handle any slot_mapping).
- *   The wavefront that holds a (sequence, kv head)'s last chunk reads the new
- *   token from k_new/v_new and writes it into its slot; nothing else in the
- *   call reads that slot.
+ *   The decode launch reads each new token from k_new/v_new; the merge
+ *   launch after it writes the rows into their slots; nothing else in the
+ *   call reads those slots.
  *
  *   k_new, v_new  [batch][kv_token_stride] bf16, first num_kv_heads*head_dim
  *                 used; kv_token_stride a multiple of 8.
