@@ -6,13 +6,14 @@
 // (sequence, kv head) pairs in order, each costing its chunks of 4*CH tokens
 // plus kPairCost units of per-pair overhead (a padding row, length 0, costs
 // only those). Every wavefront of the grid -- one work-group per CU, all
-// resident -- takes an equal contiguous range of that line and walks it,
+// resident -- takes a contiguous range of that line (of equal cost, but for
+// a smaller share on the slower odd XCDs) and walks it,
 // cutting pairs at chunk boundaries where its range starts or ends. A pair
 // that a wavefront covers entirely gets its bf16 output written directly; the
 // pieces of a pair cut by range boundaries leave (acc, max, sum) partials in
 // the workspace (at most two per wavefront: its first and its last pair), and
-// decode_merge_kernel combines them. All wavefronts get the same cost to
-// within one unit, without atomics or work queues; every work-group derives
+// decode_merge_kernel combines them. Every wavefront gets its weighted share
+// to within one unit, without atomics or work queues; every work-group derives
 // the whole partition from context_lens, which it scans into LDS. Wavefronts
 // that share a SIMD do not progress at the same rate, so each posts its
 // progress in LDS and one behind its work-group's mean raises its issue
@@ -230,7 +231,38 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
   }
   const int gw = static_cast<int>(blockIdx.x) * W + wave;
   if (gw >= nw) return;
-  const int64_t lo = C * gw / nw, hi = C * (gw + 1) / nw;
+  // Range weights: a wavefront of a work-group on an odd XCD (odd work-group
+  // index; work-group i runs on XCD i % 8) gets kWOdd / kWEven of the
+  // others' share. On MI355X the odd XCDs stream about 7% slower than the
+  // even ones (median finish times of the decode's wavefronts, every box
+  // measured), so equal shares leave them finishing last. cumw(w) is the
+  // total weight of wavefronts 0 .. w-1; wavefront w takes units
+  // [lo_of(w), lo_of(w + 1)) of the line.
+  constexpr int64_t kWEven = 16, kWOdd = 15;
+  auto cumw = [&](int64_t w) -> int64_t {
+    const int64_t i = w / W, j = w % W;
+    return W * (((i + 1) >> 1) * kWEven + (i >> 1) * kWOdd) + j * ((i & 1) ? kWOdd : kWEven);
+  };
+  const int64_t wtot = cumw(nw);
+  auto lo_of = [&](int64_t w) -> int64_t { return C * cumw(w) / wtot; };
+  // The wavefront whose range holds unit u: the largest w with
+  // lo_of(w) <= u, i.e. with cumw(w) <= t below, found by inverting cumw
+  // (pairs of work-groups weigh W * (kWEven + kWOdd) together).
+  auto wave_of = [&](int64_t u) -> int64_t {
+    const int64_t t = ((u + 1) * wtot + C - 1) / C - 1;
+    const int64_t pw = W * (kWEven + kWOdd);
+    const int64_t p = t / pw;
+    int64_t r = t - p * pw;
+    int64_t w;
+    if (r >= W * kWEven) {
+      r -= W * kWEven;
+      w = (2 * p + 1) * W + std::min<int64_t>(W - 1, r / kWOdd);
+    } else {
+      w = 2 * p * W + r / kWEven;
+    }
+    return std::min<int64_t>(w, nw - 1);
+  };
+  const int64_t lo = lo_of(gw), hi = lo_of(gw + 1);
 
   // ---- the walk over this wavefront's range -------------------------------
   int wb, wg, wL, wn, cn, started, pair_c0;
@@ -257,8 +289,8 @@ __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
       const int64_t P1 = P0 + wn + kPairCost;
       int64_t wa = 0, job = 0;
       if (P0 + kPairCost < lo && lo < P1 && hi >= P1) {
-        wa = ((P0 + kPairCost + 1) * nw - 1) / C;
-        const int64_t slot_wa = C * wa / nw >= P0 ? 0 : 1;
+        wa = wave_of(P0 + kPairCost);
+        const int64_t slot_wa = lo_of(wa) >= P0 ? 0 : 1;
         job = (gw - wa + 1) | (slot_wa << 32);
       }
       info[4 * gw + 0] = wb;
