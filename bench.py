@@ -176,7 +176,7 @@ def decode_bench(name, warmup, steps, fused=True, warm_s=0.0, flushed_only=False
     torch.cuda.synchronize()
 
     def step(i, ev):
-        if fused:  # the store fused into the decode launch
+        if fused:  # the store fused into the decode call
             if ev:
                 ev[0].record()
             pa.pa_decode_store(out, case["q"], case["k_new"], case["v_new"], case["k_cache"],
@@ -525,7 +525,7 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)} "
         f"({torch.cuda.get_device_properties(0).gcnArchName})")
 
-    log("[bench] qwen3_0.6b_decode: decode step (store fused into decode)")
+    log("[bench] qwen3_0.6b_decode: decode step (store fused into the decode call)")
     main_res = decode_bench("qwen3_0.6b_decode", args.warmup, args.steps)
     case = main_res["case"]
     digest = source_digest("decode.hip", "pa_internal.h")
@@ -548,7 +548,7 @@ def main():
     secondary = []
     if not args.no_secondary:
         for name in ("qwen3_8b_decode", "bs16_stress_decode"):
-            log(f"[bench] {name}: decode step (store fused into decode)")
+            log(f"[bench] {name}: decode step (store fused into the decode call)")
             r = decode_bench(name, max(args.warmup, SECONDARY_WARMUP), args.steps,
                              warm_s=SECONDARY_WARM_S)
             secondary.append({

@@ -292,8 +292,9 @@ int pa_sample_gumbel(int32_t* tokens, const float* probs, int64_t row_stride, in
 
 /*
  * Decode-step graphs: one HIP graph per batch-size bucket, each holding a
- * whole decode step (the launches of pa_decode_store: the step's store fused
- * into the decode kernel, then the merge) captured once and replayed with a
+ * whole decode step (the launches of pa_decode_store: the decode kernel,
+ * which reads the step's new tokens from their input rows, then the merge,
+ * which also writes them into the pools) captured once and replayed with a
  * single launch.
  * [Report] "nano-vllm 深度分析报告", section "创新之处" (graph capture at a
  * few batch sizes only, a batch rounded up to the next captured size, captured

@@ -356,7 +356,8 @@ int check_step_buffers(const pa_decode_step_buffers& b, int32_t batch) {
 }
 
 // Records the decode step for `batch` rows on `stream` (which is capturing):
-// the store fused into the decode launch, as pa_decode_store runs it.
+// the decode and merge launches with the store fused, as pa_decode_store runs
+// them.
 hipError_t record_step(const pa_decode_step_buffers& b, int32_t batch, hipStream_t stream) {
   pa::FusedStore fs;
   fs.k_new = static_cast<const uint16_t*>(b.k_new);

@@ -23,11 +23,12 @@ hipError_t launch_store_kvcache(const uint16_t* k, const uint16_t* v, int64_t kv
                                 const int32_t* slot_mapping, int32_t num_tokens,
                                 int32_t num_kv_heads, hipStream_t stream);
 
-// A store fused into a decode launch: row b's new token (position
-// context_lens[b] - 1) has its K/V in row b of k_new/v_new (token stride
-// kv_stride elements) and goes into pool slot slot_mapping[b] (-1: already in
-// the pool). k_store/v_store are the pools decode reads. No fused store when
-// slot_mapping is null.
+// A store fused into a decode (its decode and merge launches): row b's new
+// token (position context_lens[b] - 1) has its K/V in row b of k_new/v_new
+// (token stride kv_stride elements), which the decode launch reads, and goes
+// into pool slot slot_mapping[b] (-1: already in the pool), which the merge
+// launch writes. k_store/v_store are the pools decode reads. No fused store
+// when slot_mapping is null.
 struct FusedStore {
   const uint16_t* k_new = nullptr;
   const uint16_t* v_new = nullptr;
