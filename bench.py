@@ -530,8 +530,8 @@ def main():
     case = main_res["case"]
     digest = source_digest("decode.hip", "pa_internal.h")
     traffic = measured_traffic("pa_decode_store", digest)
-    roofline = {"kernel": "pa_decode_store (decode_kernel<2, 4> with the store fused, "
-                          "+ decode_merge_kernel<2>)",
+    roofline = {"kernel": "pa_decode_store (decode_kernel<2, 4> + decode_merge_kernel<2>, "
+                          "the store fused into them)",
                 "bound": "hbm", "achieved": round(main_res["decode_gbs"], 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(main_res["decode_gbs"] / HBM_PEAK_GBS, 4),
