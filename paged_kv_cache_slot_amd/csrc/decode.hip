@@ -134,10 +134,12 @@ struct Seg {
   int valid, b, g, L, t0, tend, first, last, whole, slot;
 };
 
-// Wavefronts per work-group: all that fit on a CU at once: three per SIMD for
-// G <= 2 (chunks of 4 token groups), two for G = 4, one for G = 8.
+// Wavefronts per work-group (one work-group per CU): two per SIMD for G <= 4,
+// one for G = 8 (whose registers take a whole SIMD). Three per SIMD fit at
+// G <= 2, but measured 2.2-2.3% slower: the first wavefront of each SIMD
+// finished well ahead of the other two.
 template <int G>
-constexpr int decode_waves() { return G >= 8 ? 4 : (G <= 2 ? 12 : 8); }
+constexpr int decode_waves() { return G >= 8 ? 4 : 8; }
 
 template <int G, int CH>
 __global__ __launch_bounds__(64 * decode_waves<G>(), 1) void decode_kernel(
