@@ -463,19 +463,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     if (t + 1 < num_tiles) step(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
   }
 
-  // Normalise and write. Lane holds d = db*32 + (r/4)*8 + half*4 + r%4.
+  // Normalise and write. Lane holds d = db*32 + (r/4)*8 + half*4 + r%4 of its
+  // row: written straight out, each store would put 8 bytes in each of 32
+  // rows. Instead each wavefront stages its 32 rows (bf16, 8 KB) in LDS, the
+  // stages being free once every wavefront is past the last tile, and reads
+  // them back a row per 16 lanes, so that each store writes four whole
+  // 256-byte rows. In LDS the 16-byte unit u of row r sits at u ^ (r % 16),
+  // which keeps the 8-byte writes of 32 rows to two per bank.
   const float inv = 1.f / sum_halves(lsum);
-  if (tok0 + tok < N) {
-    uint16_t* op = out + (static_cast<int64_t>(q0 + tok0 + tok) * num_q_heads + head) * kHeadDim;
+  __syncthreads();
+  uint16_t* const ostage = (wave < 2 ? lds_k0 : lds_v0) + (wave & 1) * 32 * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < kHeadDim / 32; ++db) {
+  for (int db = 0; db < kHeadDim / 32; ++db) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 w;
-        w.x = pack_bf16x2(o[db][j * 4 + 0] * inv, o[db][j * 4 + 1] * inv);
-        w.y = pack_bf16x2(o[db][j * 4 + 2] * inv, o[db][j * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + j * 8 + half * 4) = w;
-      }
+    for (int j = 0; j < 4; ++j) {
+      uint2 w;
+      w.x = pack_bf16x2(o[db][j * 4 + 0] * inv, o[db][j * 4 + 1] * inv);
+      w.y = pack_bf16x2(o[db][j * 4 + 2] * inv, o[db][j * 4 + 3] * inv);
+      const int u = db * 4 + j;  // 16-byte unit of d = db*32 + j*8 .. + 7
+      *reinterpret_cast<uint2*>(ostage + col * kHeadDim + ((u ^ (col & 15)) * 8) + half * 4) = w;
+    }
+  }
+  // Read back (LDS operations of one wavefront complete in order).
+  const int unit = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = i * 4 + (lane >> 4);  // row within the wavefront
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(ostage + r * kHeadDim + ((unit ^ (r & 15)) * 8));
+    const int rrow = wave * 32 + r;
+    const int rtok = rrow % TQ;
+    if (tok0 + rtok < N) {
+      uint16_t* op = out + (static_cast<int64_t>(q0 + tok0 + rtok) * num_q_heads + g * G +
+                            rrow / TQ) * kHeadDim;
+      *reinterpret_cast<uint4*>(op + unit * 8) = v;
     }
   }
 }
