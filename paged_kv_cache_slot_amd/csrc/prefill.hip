@@ -174,19 +174,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int hh = row / TQ;
   const int tok = row % TQ;
   const int qpos = P + tok0 + tok;                      // absolute position
-  const int qt = q0 + min(tok0 + tok, N - 1);           // clamped for loads
   const int head = g * G + hh;
   const int wave_pos0 = P + tok0 + (wave * 32) % TQ;    // lowest position of the wavefront's rows
   const int wave_pos1 = wave_pos0 + min(32, TQ) - 1;    // highest
 
-  // Q of this lane's row, the B operand of the score MFMAs as it is.
+  // Q of this lane's row, the B operand of the score MFMAs as it is; read
+  // from LDS in the first step (the rows are copied there with the first tile).
   bf16x8_t qreg[kHeadDim / 16];
-  {
-    const uint16_t* qp = q + (static_cast<int64_t>(qt) * num_q_heads + head) * kHeadDim + half * 8;
+  auto read_q = [&]() {
+    const int lr = tok * G + hh;
+    const uint16_t* qs = (lr < 64 ? lds_k1 : lds_v1) + (lr & 63) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 16; ++ks)
-      qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
-  }
+      qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qs + (((ks * 2 + half) ^ (tok & 15)) * 8));
+  };
 
   f32x16_t o[kHeadDim / 32];
 #pragma unroll
@@ -449,6 +450,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     // everyone is done with the stage that tile t+1 will overwrite.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (t == 0) {  // Q, then everyone is past it before tile 1 overwrites stage 1
+      read_q();
+      __syncthreads();
+    }
     if (t + 1 < num_tiles) issue_tile(t + 1, blk_next, kn, vn);
     tile(t, kc, vc);
     // Fetched after the tile so that no scalar load is in flight while the
@@ -456,6 +461,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     blk_next = block_of(t + 2);
   };
   issue_tile(0, block_of(0), lds_k0, lds_v0);
+  // The work-group's Q rows into stage 1 with the first tile, 1 KB per copy
+  // (the G rows of one token are contiguous in q; rows past the sequence read
+  // its last token): LDS row lr = tok * G + hh (rows 0..63 in lds_k1, 64..127
+  // in lds_v1), its 16-byte unit u at u ^ (tok % 16), so that the 32 rows one
+  // operand read covers spread over the banks. Loaded lane by lane, each
+  // instruction would take 32 bytes of each of 32 rows.
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(q + static_cast<int64_t>(q0 + tok0) * num_q_heads * kHeadDim);
+    uint16_t* const qdst = (wave < 2 ? lds_k1 : lds_v1) + (wave & 1) * 32 * kHeadDim;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int lr = wave * 32 + 4 * j + dma_row;
+      const int qtok = lr / G;
+      const int qrow = min(tok0 + qtok, N - 1) - tok0;
+      const uint32_t voff = (static_cast<uint32_t>(qrow * num_q_heads + g * G + lr % G) * kHeadDim +
+                             ((dma_unit ^ (qtok & 15)) * 8)) * 2;
+      dma16_buf(rq, voff, 0, qdst + 4 * j * kHeadDim);
+    }
+  }
   blk_next = block_of(1);
 
   for (int t = 0; t < num_tiles; t += 2) {
