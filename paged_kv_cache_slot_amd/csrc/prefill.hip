@@ -16,7 +16,11 @@
 // per lane, no registers). A wavefront copies 16 keys, which lie in one cache
 // block, from one scalar base address; keys past the context (a sequence's
 // last tile) re-read token L-1 through per-lane addresses instead. While tile
-// t is computed, tile t+1 is in flight. Inside a 256-byte row the sixteen
+// t is computed, tile t+1 is in flight. The work-group's Q rows are copied
+// into the second stage together with the first tile and moved into
+// registers in the first step; at the end each wavefront stages its output
+// rows there too, so that every global access moves whole rows. Inside a
+// 256-byte row the sixteen
 // 16-byte units are stored XOR-swizzled by the key index, so the MFMA operand
 // reads below hit distinct LDS banks.
 //
