@@ -19,10 +19,9 @@
 // t is computed, tile t+1 is in flight. The work-group's Q rows are copied
 // into the second stage together with the first tile and moved into
 // registers in the first step; at the end each wavefront stages its output
-// rows there too, so that every global access moves whole rows. Inside a
-// 256-byte row the sixteen
-// 16-byte units are stored XOR-swizzled by the key index, so the MFMA operand
-// reads below hit distinct LDS banks.
+// rows in the first stage, so that every global access moves whole rows.
+// Inside a 256-byte row the sixteen 16-byte units are stored XOR-swizzled by
+// the key index, so the MFMA operand reads below hit distinct LDS banks.
 //
 // Per wavefront and tile, flash-attention style, in log2 units:
 //   S^T = K Q^T      bf16 MFMA 32x32x16, fp32 accumulate: each lane holds the
