@@ -67,7 +67,8 @@ constexpr int64_t kFillWaves = 2048;   // working wavefronts that keep HBM strea
 constexpr float kLazyLog2 = 8.f;       // headroom of the softmax reference (log2 units)
 constexpr int kRecord = 132;           // floats per partial record: acc[128], max, sum, pad
 constexpr int kInfoOffset = 64;        // workspace bytes before the per-wavefront records
-constexpr int kMergeWaves = 16;        // wavefronts per work-group of the merge
+constexpr int kMergeWaves = 4;         // wavefronts per work-group of the merge (small groups
+                                       // spread its latency-bound jobs over every CU)
 
 // Working wavefronts for a cost line of C units, before the grid's cap. A
 // wavefront is given kFullUnits units; when that leaves fewer than kFillWaves
