@@ -6,12 +6,14 @@
 One step = one pass of the hot path over one synthetic batch of the
 Qwen3-0.6B-shaped decode workload (256 sequences, context lengths uniform in
 [100, 2048], 16 query / 8 KV heads, head_dim 128, block_size 256, physical
-blocks randomly permuted): pa_store_kvcache of the 256 new tokens, then
-pa_decode. Inputs are resident in HBM before timing starts. The headline
-`value` is algorithmic bytes moved per step / step time (GB/s).
+blocks randomly permuted): one pa_decode_store call, which writes the 256 new
+tokens' K/V into the pools and attends over the paged contexts. Inputs are
+resident in HBM before timing starts. The headline `value` is algorithmic
+bytes moved per step / step time (GB/s).
 
 The same JSON line carries:
-  roofline      for pa_decode (split-K attention kernel + its reduce pass),
+  roofline      for pa_decode_store (the stream-K attention kernel + its
+                merge pass, which also writes the new tokens into the pools),
                 timed with HIP events around each call on the launch stream;
   cpu_baseline  the CPU oracle (fp64) on the same step, on the host cores;
   secondary     the other workloads of the pages: Qwen3-8B-shaped decode
@@ -25,7 +27,10 @@ The same JSON line carries:
                 vocabulary (GB/s of probabilities against HBM peak);
   decode_graphs wall time per decode step replayed from HIP graphs against
                 the eager launches, at batches 1 .. 256, for dependent
-                (wait after every step) and pipelined steps.
+                (wait after every step) and pipelined steps;
+  mfma_ceiling  a library bf16 GEMM (torch.mm, 8192^3) on random and on
+                zero operands: what the matrix cores sustain at the clock
+                the chip holds under real data, beside the prefill figure.
 Progress goes to stderr; stdout holds only the JSON line.
 """
 import argparse
@@ -248,6 +253,45 @@ def prefill_bench(warmup, steps, warm_s=0.0):
     kern_ms = float(np.mean(kms))
     return dict(ms_per_step=ms, flops=flops, prefill_ms=kern_ms,
                 tflops=flops / (kern_ms * 1e-3) / 1e12, total_q=case["total_q"])
+
+
+def mfma_ceiling_bench(warmup, steps, n=8192, warm_s=0.0):
+    """A plain bf16 GEMM from the vendor library (torch.mm, C = A B with
+    contiguous n x n operands), timed like the prefill leg, once on N(0,1)
+    operands and once on zeros. Not part of the hot path: it shows the MFMA
+    rate the chip sustains at the clock it holds under real data (zero
+    operands draw less power, so the chip clocks higher), the practical
+    ceiling beside the nominal peak."""
+    import torch
+    import numpy as np
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    flops = 2.0 * n ** 3
+    res = {"shape": f"bf16 [{n},{n}] x [{n},{n}]"}
+    for kind in ("random", "zeros"):
+        if kind == "zeros":
+            a.zero_()
+            b.zero_()
+        torch.cuda.synchronize()
+
+        def step(i, ev):
+            if ev:
+                ev[0].record()
+            torch.mm(a, b, out=c)
+            if ev:
+                ev[1].record()
+
+        _, kms = run_timed(step, warmup, steps, warm_s)
+        med = float(np.median(kms))
+        res[f"{kind}_us"] = round(med * 1e3, 2)
+        res[f"{kind}_TFLOPs"] = round(flops / (med * 1e-3) / 1e12, 2)
+        res[f"{kind}_frac_mfma"] = round(flops / (med * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return res
 
 
 def block_manager_bench(decode_steps=256, oracle_steps=8):
@@ -476,7 +520,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-leg", choices=["prefill", "sampler", "decode", "decode-flushed",
-                                              "graphs"],
+                                              "graphs", "mfma-ceiling"],
                     default=None,
                     help="only run this leg and print its own result (for counter runs and "
                          "kernel traces under rocprofv3); the benchmark line is not printed")
@@ -516,7 +560,10 @@ def main():
                                                      max(args.warmup, SECONDARY_WARMUP),
                                                      args.steps, warm_s=SECONDARY_WARM_S,
                                                      flushed_only=True),
-              "graphs": lambda: graph_bench(batches=(args.batch,))}[args.profile_leg]
+              "graphs": lambda: graph_bench(batches=(args.batch,)),
+              "mfma-ceiling": lambda: mfma_ceiling_bench(max(args.warmup, SECONDARY_WARMUP),
+                                                         args.steps, warm_s=SECONDARY_WARM_S)
+              }[args.profile_leg]
         res = fn()
         print(json.dumps({k: v for k, v in res.items() if k != "case"},
                          default=lambda x: x.tolist() if hasattr(x, "tolist") else str(x)),
@@ -573,12 +620,18 @@ def main():
             "algorithmic_flops": r["flops"], "total_q": r["total_q"]})
         torch.cuda.empty_cache()
 
-    graphs = sampler = None
+    graphs = sampler = ceiling = None
     if not args.no_secondary:
         log("[bench] gumbel-max sampler")
         sampler = sampler_bench(args.warmup, args.steps)
         log("[bench] decode-step graphs vs eager")
         graphs = graph_bench()
+        log("[bench] library bf16 GEMM (MFMA ceiling under real data)")
+        ceiling = mfma_ceiling_bench(max(args.warmup, SECONDARY_WARMUP), args.steps,
+                                     warm_s=SECONDARY_WARM_S)
+        pf = next(x for x in secondary if x["workload"] == "qwen3_8b_prefill_prefix")
+        ceiling["prefill_over_gemm_random"] = round(pf["prefill_TFLOPs"]
+                                                    / ceiling["random_TFLOPs"], 4)
 
     log("[bench] block manager (host)")
     bmr = block_manager_bench()
@@ -606,6 +659,7 @@ def main():
                    "step_bytes": main_res["step_bytes"]},
         "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
         "block_manager": bmr, "decode_graphs": graphs, "sampler": sampler,
+        "mfma_ceiling": ceiling,
     }
     print(json.dumps(line), flush=True)
 
