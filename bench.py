@@ -118,6 +118,7 @@ def prefill_flops(case):
 # seconds of them. Measured in a fresh process, the Qwen3-8B decode steps get
 # faster over the first seconds of GPU work (389 -> 363 us over four 20-step
 # runs), so a few warm-up steps leave those legs below their steady state.
+ORACLE_SECONDS = 10.0  # host time the decode oracle baseline runs for
 SECONDARY_WARMUP = 10
 SECONDARY_WARM_S = 0.5
 
@@ -252,7 +253,7 @@ def prefill_bench(warmup, steps, warm_s=0.0):
     flops = prefill_flops(case)
     kern_ms = float(np.mean(kms))
     return dict(ms_per_step=ms, flops=flops, prefill_ms=kern_ms,
-                tflops=flops / (kern_ms * 1e-3) / 1e12, total_q=case["total_q"])
+                tflops=flops / (kern_ms * 1e-3) / 1e12, total_q=case["total_q"], case=case)
 
 
 def mfma_ceiling_bench(warmup, steps, n=8192, warm_s=0.0):
@@ -497,19 +498,56 @@ def cpu_baseline(case):
     slots = case["slot_mapping"].cpu().numpy()
     bt, cl = case["block_table"].cpu().numpy(), case["context_lens"].cpu().numpy()
     q = u16(case["q"])
+    # The whole step, repeated until about 10 s of host time have passed (the
+    # store rewrites the same rows each time).
+    reps = 0
     t0 = time.perf_counter()
-    oracle.store_kvcache(kn, vn, kc, vc, slots, case["block_size"], inplace=True)
-    oracle.decode(q, kc, vc, bt, cl, case["scale"], nthreads=nthreads)
+    while reps < 1 or (time.perf_counter() - t0 < ORACLE_SECONDS and reps < 256):
+        oracle.store_kvcache(kn, vn, kc, vc, slots, case["block_size"], inplace=True)
+        oracle.decode(q, kc, vc, bt, cl, case["scale"], nthreads=nthreads)
+        reps += 1
     dt = time.perf_counter() - t0
     nbytes = decode_bytes(case) + store_bytes(case)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
-            "kind": "oracle", "seconds": round(dt, 3),
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+            "kind": "oracle", "seconds": round(dt, 3), "steps": reps,
             "host": {"nproc": os.cpu_count(), "hardware_concurrency": hw,
                      "affinity_cpus": affinity,
                      "threads_used": f"min(hardware_concurrency, affinity, 16) = {nthreads}"},
-            "sample": f"the whole step once: store of {case['batch']} new tokens + fp64 "
-                      f"attention for all {case['batch']} rows x {case['num_q_heads']} heads "
-                      f"(qwen3_0.6b_decode, {int(np.asarray(case['lens']).sum())} context tokens)"}
+            "sample": f"the whole step, {reps} times back to back: store of {case['batch']} new "
+                      f"tokens + fp64 attention for all {case['batch']} rows x "
+                      f"{case['num_q_heads']} heads (qwen3_0.6b_decode, "
+                      f"{int(np.asarray(case['lens']).sum())} context tokens)"}
+
+
+def cpu_prefill_baseline(case, sequences=8):
+    """The oracle (plain fp64 C++) on the first `sequences` sequences of the
+    prefill workload (store of their new tokens, then causal attention over
+    prefix + new tokens), on the host cores: TFLOP/s of algorithmic flops."""
+    import numpy as np
+    import torch
+    import oracle
+    nthreads = min(oracle.hardware_threads(), len(os.sched_getaffinity(0)), 16)
+    u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    cu = case["cu_seqlens_q"].cpu().numpy()
+    n = min(sequences, len(cu) - 1)
+    rows = int(cu[n])
+    kc, vc = u16(case["k_cache"]), u16(case["v_cache"])
+    kn, vn = u16(case["k_new"])[:rows], u16(case["v_new"])[:rows]
+    slots = case["slot_mapping"].cpu().numpy()[:rows]
+    q = u16(case["q"])[:rows]
+    cl = case["context_lens"].cpu().numpy()[:n]
+    bt = case["block_table"].cpu().numpy()[:n]
+    N = np.diff(cu[:n + 1]).astype(np.int64)
+    P = cl.astype(np.int64) - N
+    flops = 4 * case["num_q_heads"] * case["head_dim"] * int((N * P + N * (N + 1) // 2).sum())
+    t0 = time.perf_counter()
+    oracle.store_kvcache(kn, vn, kc, vc, slots, case["block_size"], inplace=True)
+    oracle.prefill(q, kc, vc, cu[:n + 1], cl, bt, case["scale"], nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"TFLOPs": round(flops / dt / 1e12, 5), "cores": nthreads, "kind": "oracle",
+            "seconds": round(dt, 3), "algorithmic_flops": flops,
+            "sample": f"sequences 0..{n - 1} of qwen3_8b_prefill_prefix ({rows} new tokens "
+                      f"after {int(P.sum())} cached), store + fp64 causal attention, once"}
 
 
 def main():
@@ -618,6 +656,12 @@ def main():
             "prefill_TFLOPs": round(r["tflops"], 2),
             "prefill_frac_mfma": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops": r["flops"], "total_q": r["total_q"]})
+        if not args.no_cpu_baseline:
+            log("[bench] prefill oracle on a sample of the sequences")
+            po = cpu_prefill_baseline(r["case"])
+            po["gpu_over_oracle"] = round(r["tflops"] / po["TFLOPs"], 1)
+            secondary[-1]["oracle"] = po
+        del r
         torch.cuda.empty_cache()
 
     graphs = sampler = ceiling = None
@@ -642,6 +686,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(case)
+        cpu["gpu_over_oracle"] = round(main_res["gbs"] / cpu["value"], 1)
 
     line = {
         "metric": METRIC, "value": round(main_res["gbs"], 2), "unit": "GB/s", "n_gpus": 1,
