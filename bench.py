@@ -256,6 +256,72 @@ def prefill_bench(warmup, steps, warm_s=0.0):
                 tflops=flops / (kern_ms * 1e-3) / 1e12, total_q=case["total_q"], case=case)
 
 
+def prefill_lengths_bench(warmup, steps, warm_s=0.0,
+                          lengths=(512, 1024, 2048, 4096, 8192, 16384), tokens=32768):
+    """pa_prefill_varlen against prompt length: for each N, tokens // N
+    sequences of N new tokens and no cached prefix (32 q / 8 kv heads,
+    head_dim 128, block_size 256), algorithmic TFLOP/s. Beside it, torch's
+    flash attention (forced flash backend, dense causal, K/V heads expanded)
+    on the same shapes, for context; it is not part of the hot path."""
+    import torch
+    import numpy as np
+    import paged_kv_cache_slot_amd as pa
+    import workloads
+    import torch.nn.functional as F
+    rows = []
+    for n in lengths:
+        b = max(1, tokens // n)
+        case = workloads.prefill_case(b, (n, n), 32, 8, 128, 256, seed=500 + n, device="cuda",
+                                      chains=1, chain_blocks=1, new_lens=[n] * b,
+                                      prefix_blocks=[0] * b, prefix_chain=[0] * b)
+        pa.pa_store_kvcache(case["k_new"], case["v_new"], case["k_cache"], case["v_cache"],
+                            case["slot_mapping"])
+        out = torch.empty_like(case["q"])
+        torch.cuda.synchronize()
+
+        def step(i, ev):
+            if ev:
+                ev[0].record()
+            pa.pa_prefill_varlen(out, case["q"], case["k_cache"], case["v_cache"],
+                                 case["cu_seqlens_q"], case["context_lens"], case["block_table"],
+                                 case["max_seqlen_q"], case["scale"])
+            if ev:
+                ev[1].record()
+
+        _, kms = run_timed(step, warmup, steps, warm_s)
+        flops = 4 * 32 * 128 * b * n * (n + 1) // 2
+        us = float(np.median(kms)) * 1e3
+        row = {"new_tokens": n, "sequences": b, "prefill_us": round(us, 1),
+               "prefill_TFLOPs": round(flops / us / 1e6, 1),
+               "prefill_frac_mfma": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        try:
+            from torch.nn.attention import sdpa_kernel, SDPBackend
+            q = case["q"].view(b, n, 32, 128).transpose(1, 2).contiguous()
+            k = case["k_new"].view(b, n, 8, 128).transpose(1, 2).repeat_interleave(4, 1).contiguous()
+            v = case["v_new"].view(b, n, 8, 128).transpose(1, 2).repeat_interleave(4, 1).contiguous()
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                def tstep(i, ev):
+                    if ev:
+                        ev[0].record()
+                    F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=case["scale"])
+                    if ev:
+                        ev[1].record()
+                _, tms = run_timed(tstep, warmup, steps, warm_s)
+            tus = float(np.median(tms)) * 1e3
+            row["torch_flash_us"] = round(tus, 1)
+            row["torch_flash_TFLOPs"] = round(flops / tus / 1e6, 1)
+            del q, k, v
+        except (RuntimeError, ImportError) as e:  # no flash backend in this torch build
+            row["torch_flash_us"] = None
+            row["torch_flash_note"] = str(e)[:120]
+        log(f"[bench] prefill {b} x {n}: {row}")
+        rows.append(row)
+        del case, out
+        torch.cuda.empty_cache()
+    return {"shape": "32 q / 8 kv heads, head_dim 128, block_size 256, no cached prefix",
+            "rows": rows}
+
+
 def mfma_ceiling_bench(warmup, steps, n=8192, warm_s=0.0):
     """A plain bf16 GEMM from the vendor library (torch.mm, C = A B with
     contiguous n x n operands), timed like the prefill leg, once on N(0,1)
@@ -558,7 +624,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-leg", choices=["prefill", "sampler", "decode", "decode-flushed",
-                                              "graphs", "mfma-ceiling"],
+                                              "graphs", "mfma-ceiling", "prefill-lengths"],
                     default=None,
                     help="only run this leg and print its own result (for counter runs and "
                          "kernel traces under rocprofv3); the benchmark line is not printed")
@@ -600,7 +666,9 @@ def main():
                                                      flushed_only=True),
               "graphs": lambda: graph_bench(batches=(args.batch,)),
               "mfma-ceiling": lambda: mfma_ceiling_bench(max(args.warmup, SECONDARY_WARMUP),
-                                                         args.steps, warm_s=SECONDARY_WARM_S)
+                                                         args.steps, warm_s=SECONDARY_WARM_S),
+              "prefill-lengths": lambda: prefill_lengths_bench(
+                  max(args.warmup, SECONDARY_WARMUP), args.steps, warm_s=SECONDARY_WARM_S),
               }[args.profile_leg]
         res = fn()
         print(json.dumps({k: v for k, v in res.items() if k != "case"},
