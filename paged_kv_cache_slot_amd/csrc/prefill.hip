@@ -367,17 +367,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       }
       tsum = (t[0] + t[1]) + (t[2] + t[3]);
     };
-    // Moves the reference up to the row maximum where that is higher (to it in
-    // any case on the first tile), rescales the state and recomputes P.
-    auto raise_reference = [&](bool first) {
+    // The row's maximum of s - mc over this tile's visible keys.
+    auto row_max = [&]() {
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
-      tmax = max_halves(tmax);  // the row's max of s - mc
-      const float d = first ? tmax : fmaxf(tmax, 0.f);
-      const float alpha = first ? 1.f : fast_exp2(-d);  // o and lsum are still 0 on the first
+      return max_halves(tmax);
+    };
+    // Moves the reference up to the row maximum where that is higher,
+    // rescales the state and recomputes P.
+    auto raise_reference = [&]() {
+      const float d = fmaxf(row_max(), 0.f);
+      const float alpha = fast_exp2(-d);
       mc += d;
       lsum *= alpha;
 #pragma unroll
@@ -390,11 +393,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         for (int r = 0; r < 16; ++r) s[kb][r] -= d;
       make_p();
     };
+    // The first tile sets the reference to its row maximum (every row sees
+    // key 0, so it is finite) before any exponential is taken.
+    if (t == 0) {
+      const float m0 = row_max();
+      mc = m0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= m0;
+    }
     make_p();
     // The sum test also catches an overflow to infinity. Per lane: each half
-    // of a row stays below the bound, the row below twice it. The first tile
-    // always sets the reference (one call site keeps register use down).
-    if (t == 0 || __any(!(tsum <= kRescaleSum))) raise_reference(t == 0);
+    // of a row stays below the bound, the row below twice it.
+    if (t != 0 && __any(!(tsum <= kRescaleSum))) raise_reference();
     lsum += tsum;
 
     // V^T operands: two transposed reads per (32-row block db, 16-key step ks).
