@@ -1,4 +1,4 @@
-// Stress driver for the CPU oracle (oracle/oracle.cpp), built with host
+// Stress program for the CPU oracle (oracle/oracle.cpp), built with host
 // sanitizers by tests/test_oracle_sanitized.py. Random small cases drive
 // oracle_store_kvcache, oracle_decode and oracle_prefill: padding rows
 // (length 0), -1 slots, ragged lengths, row subsets, several block sizes,
