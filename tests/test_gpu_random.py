@@ -1,7 +1,8 @@
 """Seeded random shapes against the oracle: head groupings G = 1..8, kv head
-counts 1..8, block sizes 16..256, batch sizes, lengths with empty rows mixed
-in, and softmax scales between 0.02 and 1, drawn once from fixed seeds (the
-test ids name each draw). Decode: the fused step (pa_decode_store) on every
+counts 1..8, block sizes 16..256, batch sizes (up to 200 rows), lengths (up to
+8000 tokens) with empty rows mixed in, cached prefixes of up to 6 blocks, and
+softmax scales between 0.02 and 1, drawn once from fixed seeds (the test ids
+name each draw). Decode: the fused step (pa_decode_store) on every
 row against the oracle, both pools bit for bit against the oracle's store,
 and the separate store + decode bit for bit against the fused step. Prefill:
 store + prefill over cached prefixes, every row against the oracle.
@@ -29,42 +30,46 @@ def _heads(rng):
             return g * hkv, hkv
 
 
-def _decode_draws(n, seed):
+def _decode_draws(n, seed, data_seed, max_batch=48, max_len=3000, tag="d"):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         hq, hkv = _heads(rng)
         bs = int(rng.choice(BLOCK_SIZES))
-        batch = int(rng.integers(1, 49))
-        lens = rng.integers(1, 3001, size=batch)
+        batch = int(rng.integers(1, max_batch + 1))
+        lens = rng.integers(1, max_len + 1, size=batch)
         lens[rng.random(batch) < 0.1] = 0
         scale = float(np.float32(np.exp(rng.uniform(np.log(0.02), 0.0))))
         extra = int(rng.choice([0, 0, 7, 300]))  # max_context_len above the longest row
-        out.append((f"d{i}-hq{hq}-hkv{hkv}-bs{bs}-b{batch}", hq, hkv, bs, [int(x) for x in lens],
-                    scale, extra, 2000 + i))
+        out.append((f"{tag}{i}-hq{hq}-hkv{hkv}-bs{bs}-b{batch}", hq, hkv, bs,
+                    [int(x) for x in lens], scale, extra, data_seed + i))
     return out
 
 
-def _prefill_draws(n, seed):
+def _prefill_draws(n, seed, data_seed, max_new=300, max_pre=3, tag="p"):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         hq, hkv = _heads(rng)
         bs = int(rng.choice(BLOCK_SIZES))
         batch = int(rng.integers(1, 7))
-        new = rng.integers(1, 301, size=batch)
+        new = rng.integers(1, max_new + 1, size=batch)
         new[rng.random(batch) < 0.15] = 0
         if new.sum() == 0:  # at least one row to check
-            new[0] = int(rng.integers(1, 301))
-        pre = rng.integers(0, 4, size=batch)
+            new[0] = int(rng.integers(1, max_new + 1))
+        pre = rng.integers(0, max_pre + 1, size=batch)
         scale = float(np.float32(np.exp(rng.uniform(np.log(0.02), 0.0))))
-        out.append((f"p{i}-hq{hq}-hkv{hkv}-bs{bs}-b{batch}", hq, hkv, bs, [int(x) for x in new],
-                    [int(x) for x in pre], scale, 3000 + i))
+        out.append((f"{tag}{i}-hq{hq}-hkv{hkv}-bs{bs}-b{batch}", hq, hkv, bs,
+                    [int(x) for x in new], [int(x) for x in pre], scale, data_seed + i))
     return out
 
 
-DECODE_DRAWS = _decode_draws(8, 71)
-PREFILL_DRAWS = _prefill_draws(6, 72)
+# Two sets each: short contexts and small batches, then longer contexts (up to
+# 8000 tokens), larger batches (up to 200 rows) and longer prefixes.
+DECODE_DRAWS = (_decode_draws(8, 71, 2000)
+                + _decode_draws(8, 73, 4000, max_batch=200, max_len=8000, tag="D"))
+PREFILL_DRAWS = (_prefill_draws(6, 72, 3000)
+                 + _prefill_draws(6, 74, 5000, max_new=600, max_pre=6, tag="P"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -119,7 +124,8 @@ def test_decode_step_random(cid, hq, hkv, bs, lens, scale, extra, seed):
 def test_prefill_random(cid, hq, hkv, bs, new, pre, scale, seed):
     say(f"[case] random prefill {cid}: new={new} prefix_blocks={pre} scale={scale} seed={seed}")
     h = workloads.prefill_case(len(new), (1, 300), hq, hkv, 128, bs, seed=seed, device="cpu",
-                               chains=3, chain_blocks=3, new_lens=new, prefix_blocks=pre)
+                               chains=3, chain_blocks=max(3, max(pre)), new_lens=new,
+                               prefix_blocks=pre)
     h["scale"] = scale
     case = to_device(host_copy(h))
     gpu_store(case)
